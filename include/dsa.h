@@ -1,0 +1,194 @@
+/*
+ * dsa.h -- C ABI of the MI355X (gfx950) DeepSeek Sparse Attention hot path.
+ *
+ * The path has three steps, each exported on its own and fused in
+ * dsa_forward:
+ *   1. index scores  (lightning indexer: HF model doc "DeepSeek-V3.2",
+ *      section "DeepSeek Sparse Attention (DSA)", item 1, and the paragraph on
+ *      the single-head index-key cache that follows the list),
+ *   2. per-query top-k selection (same section, item 2; index_topk in the
+ *      released configuration excerpt of the atlas "DeepSeek-V3.2-Exp"
+ *      token-ids page),
+ *   3. sparse MLA attention in absorbed MQA form over the chosen latent rows
+ *      (item 2; altools.ai "Technical Principles": MLA with MQA, key entries
+ *      shared across query heads; visual-learn "DeepSeek-V3.2 / Exp",
+ *      "Different questions select different tokens": the cache holds MLA's
+ *      compressed vectors).
+ *
+ * Conventions shared by every entry point
+ *   - Every tensor pointer is a caller-owned DEVICE pointer to a contiguous
+ *     row-major array with the layout given below, 16-byte aligned.  The
+ *     library never allocates, frees or keeps memory; temporary memory comes
+ *     from a caller workspace sized by dsa_workspace_size().
+ *   - Calls are asynchronous on `stream` (hipStream_t; 0 = the null stream):
+ *     the caller keeps every buffer alive until the stream has passed the
+ *     call.  No host synchronisation happens inside the library.
+ *   - Argument checks run before any HIP call; on a failed check nothing is
+ *     launched and the status says why.  Launch failures are reported as
+ *     DSA_ERR_HIP.  No C++ exception crosses this interface.  After an error
+ *     the contents of output buffers are undefined.
+ *   - Query i of sequence b sits at position p = kv_len - q_len + i and sees
+ *     keys 0..p (n = p + 1 of them): the causal mask keeps the diagonal
+ *     (atlas token-ids page, transformer-forward excerpt), and a single decode
+ *     query sees the whole cache.
+ *   - The library keeps no mutable global state: calls on different streams
+ *     or host threads are independent.
+ */
+#ifndef DSA_H_
+#define DSA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define DSA_ABI_VERSION 1
+
+typedef enum {
+  DSA_OK = 0,
+  DSA_ERR_INVALID_ARGUMENT = 1,   /* null pointer, bad size, misalignment */
+  DSA_ERR_UNSUPPORTED = 2,        /* valid request this build has no kernel for */
+  DSA_ERR_WORKSPACE_TOO_SMALL = 3,
+  DSA_ERR_HIP = 4                 /* a HIP runtime call or launch failed */
+} dsa_status_t;
+
+typedef enum {
+  DSA_F32 = 0,
+  DSA_BF16 = 1,
+  DSA_FP8_E4M3 = 2                /* OCP E4M3 ("fn"): bias 7, max 448, no inf */
+} dsa_dtype_t;
+
+/* Problem description shared by all entry points. */
+typedef struct {
+  int32_t batch;        /* B sequences                                        */
+  int32_t q_len;        /* Lq queries per sequence (1 for decode)             */
+  int32_t kv_len;       /* Lk cached tokens per sequence, Lk >= Lq            */
+  int32_t index_heads;  /* H index heads (index_n_heads, 64 in V3.2)          */
+  int32_t index_dim;    /* D index head dim (index_head_dim, 128 in V3.2)     */
+  int32_t topk;         /* K (index_topk, 2048 in V3.2)                       */
+  int32_t attn_heads;   /* NH query heads of MLA (n_heads, 128 in V3.2)       */
+  int32_t qk_dim;       /* Dqk = kv_lora_rank + qk_rope_head_dim (576)        */
+  int32_t v_dim;        /* Dv = kv_lora_rank (512): values are the leading
+                           Dv dims of each kv row (absorbed form)            */
+  float softmax_scale;  /* multiplies q.k before the softmax                  */
+  dsa_dtype_t index_dtype;  /* q_idx / k_idx element type                     */
+  dsa_dtype_t attn_dtype;   /* q_attn / kv element type                       */
+  dsa_dtype_t out_dtype;    /* out element type                               */
+} dsa_problem_t;
+
+/* Supported dtype combinations (anything else: DSA_ERR_UNSUPPORTED)
+ *   index F32      + attn F32  + out F32         any dims within the limits below
+ *   index BF16     + attn BF16 + out BF16|F32    H = 64, D = 128, NH = 128, Dqk = 576, Dv = 512
+ *   index FP8_E4M3 + attn BF16 + out BF16|F32    same dims; q_scale/k_scale required
+ * F32 limits: H*D <= 8192, Dqk <= 1024, Dv <= 1024, K <= 4096.
+ * All paths: K >= 1, Lq >= 1, Lk >= Lq, Lk <= 2^24 (scores rows in 32-bit indices).
+ */
+
+/* Step 1: index scores.
+ *   q_idx   [B][Lq][H][D]  index_dtype (FP8: E4M3 codes, one byte each)
+ *   q_scale [B][Lq][H]     uint8 ue8m0 exponents, scale = 2^(e-127); FP8 only,
+ *                          else NULL.  One scale per 128-element row.
+ *   k_idx   [B][Lk][D]     index_dtype, the single-head index-key cache
+ *   k_scale [B][Lk]        uint8 ue8m0 exponents; FP8 only, else NULL
+ *   head_w  [B][Lq][H]     fp32 per-query head weights (any sign)
+ *   scores  [B][Lq][Lk]    fp32 out:
+ *       scores[b][i][s] = sum_h w[h] * max(0, q_h . k_s)   for s <= p
+ *                       = -inf                              for s >  p
+ *   With FP8 inputs q_h and k_s are the dequantised values code * scale;
+ *   accumulation is fp32.
+ */
+dsa_status_t dsa_index_scores(const dsa_problem_t* prob,
+                              const void* q_idx, const uint8_t* q_scale,
+                              const void* k_idx, const uint8_t* k_scale,
+                              const float* head_w, float* scores,
+                              hipStream_t stream);
+
+/* Step 2: exact per-row top-k.
+ *   scores   fp32 rows, row (b, i) starts at scores + (b*Lq + i) * row_stride;
+ *            only its first n = Lk - Lq + i + 1 entries are read.
+ *            row_stride >= Lk (elements).  NaN inputs are not supported.
+ *   topk_idx [B][Lq][K] int32 out: the K' = min(K, n) positions with the
+ *            largest scores, larger score first and lower position first
+ *            among equal scores (+0.0 == -0.0), written in ascending
+ *            position order and padded with -1.  Bit-exact: the result is a
+ *            pure function of the fp32 bit patterns.
+ */
+dsa_status_t dsa_topk(const dsa_problem_t* prob, const float* scores, int64_t row_stride,
+                      int32_t* topk_idx, hipStream_t stream);
+
+/* Step 3: sparse MLA attention over the chosen rows (absorbed MQA form).
+ *   q_attn   [B][Lq][NH][Dqk] attn_dtype
+ *   kv       [B][Lk][Dqk]     attn_dtype; one latent row per token, shared
+ *                             by all NH heads; values = its leading Dv dims
+ *   topk_idx [B][Lq][K]       int32 positions; entries < 0 are skipped; every
+ *                             entry >= 0 must be < Lk (not checked on device);
+ *                             each row must hold at least one entry >= 0
+ *   out      [B][Lq][NH][Dv]  out_dtype:
+ *       out[a] = sum_j softmax_j(scale * q_a . kv_j) * kv_j[0:Dv] over chosen j
+ *   lse      [B][Lq][NH] fp32 natural-log sum-exp of the scaled logits, or NULL
+ *   workspace / workspace_bytes: at least dsa_workspace_size(prob, DSA_OP_ATTN)
+ *            bytes (may be 0 bytes / NULL when that size is 0).
+ */
+dsa_status_t dsa_sparse_mla_attn(const dsa_problem_t* prob,
+                                 const void* q_attn, const void* kv, const int32_t* topk_idx,
+                                 void* out, float* lse,
+                                 void* workspace, size_t workspace_bytes,
+                                 hipStream_t stream);
+
+/* Steps 1-3 fused in stream order (scores never leave the workspace).
+ *   Tensors as above.  topk_idx may be NULL (then the indices live only in
+ *   the workspace); if given it receives the selected positions.  lse may be
+ *   NULL.  workspace: at least dsa_workspace_size(prob, DSA_OP_FORWARD) bytes.
+ */
+dsa_status_t dsa_forward(const dsa_problem_t* prob,
+                         const void* q_idx, const uint8_t* q_scale,
+                         const void* k_idx, const uint8_t* k_scale,
+                         const float* head_w,
+                         const void* q_attn, const void* kv,
+                         int32_t* topk_idx, void* out, float* lse,
+                         void* workspace, size_t workspace_bytes,
+                         hipStream_t stream);
+
+/* dsa_forward with per-kernel timing events (for measurement).
+ *   events: caller-created hipEvent_t handles, 2 per launch slot:
+ *     events[2*(c*DSA_NUM_STAGES + s)] recorded before, and
+ *     events[2*(c*DSA_NUM_STAGES + s) + 1] after, the launch of stage s for
+ *     query chunk c, for c < n_event_slots / (2*DSA_NUM_STAGES).  Stages
+ *     that do not run in a chunk record both events back to back.
+ *   n_chunks_out: if not NULL, receives the number of query chunks used.
+ */
+#define DSA_NUM_STAGES 4   /* 0 indexer, 1 top-k, 2 attention, 3 split combine */
+dsa_status_t dsa_forward_timed(const dsa_problem_t* prob,
+                               const void* q_idx, const uint8_t* q_scale,
+                               const void* k_idx, const uint8_t* k_scale,
+                               const float* head_w,
+                               const void* q_attn, const void* kv,
+                               int32_t* topk_idx, void* out, float* lse,
+                               void* workspace, size_t workspace_bytes,
+                               hipEvent_t* events, int32_t n_event_slots,
+                               int32_t* n_chunks_out,
+                               hipStream_t stream);
+
+#define DSA_OP_ATTN 1
+#define DSA_OP_FORWARD 2
+/* Workspace bytes needed by dsa_sparse_mla_attn (op = DSA_OP_ATTN) or
+ * dsa_forward (op = DSA_OP_FORWARD) for this problem; 0 for an invalid
+ * problem or op.  Pure host function, no HIP call. */
+size_t dsa_workspace_size(const dsa_problem_t* prob, int32_t op);
+
+/* Number of query chunks dsa_forward splits this problem into (host only). */
+int32_t dsa_forward_chunks(const dsa_problem_t* prob);
+
+/* Static description of a status code. */
+const char* dsa_status_string(dsa_status_t status);
+
+/* DSA_ABI_VERSION of the built library. */
+int32_t dsa_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* DSA_H_ */

@@ -1,0 +1,311 @@
+// C-ABI front end of the DSA library: argument checks, workspace carving,
+// query chunking and kernel dispatch.  No allocation, no host sync, no
+// mutable global state.
+#include "dsa.h"
+#include "dsa_internal.h"
+
+#include <cmath>
+#include <cstdint>
+
+using namespace dsa;
+
+namespace {
+
+constexpr size_t kAlign = 256;
+constexpr size_t kScoresBudget = size_t(256) << 20;   // bytes of scores per query chunk
+constexpr int64_t kMaxLk = int64_t(1) << 24;
+
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+bool is_v32_dims_index(const dsa_problem_t& p) { return p.index_heads == 64 && p.index_dim == 128; }
+bool is_v32_dims_attn(const dsa_problem_t& p) {
+  return p.attn_heads == 128 && p.qk_dim == 576 && p.v_dim == 512;
+}
+
+enum Path { kPathF32, kPathBF16, kPathFP8 };
+
+// Shape and dtype checks shared by every entry point.
+dsa_status_t check_problem(const dsa_problem_t* p, Path* path) {
+  if (!p) return DSA_ERR_INVALID_ARGUMENT;
+  if (p->batch < 1 || p->q_len < 1 || p->kv_len < p->q_len || p->kv_len > kMaxLk) return DSA_ERR_INVALID_ARGUMENT;
+  if (p->index_heads < 1 || p->index_dim < 1 || p->topk < 1) return DSA_ERR_INVALID_ARGUMENT;
+  if (p->attn_heads < 1 || p->qk_dim < 1 || p->v_dim < 1 || p->v_dim > p->qk_dim) return DSA_ERR_INVALID_ARGUMENT;
+  if (!std::isfinite(p->softmax_scale)) return DSA_ERR_INVALID_ARGUMENT;
+  const int it = p->index_dtype, at = p->attn_dtype, ot = p->out_dtype;
+  if (it < DSA_F32 || it > DSA_FP8_E4M3 || at < DSA_F32 || at > DSA_FP8_E4M3 || ot < DSA_F32 || ot > DSA_FP8_E4M3)
+    return DSA_ERR_INVALID_ARGUMENT;
+  if (it == DSA_F32 && at == DSA_F32 && ot == DSA_F32) {
+    if ((int64_t)p->index_heads * p->index_dim > 8192 || p->qk_dim > 1024 || p->v_dim > 1024 || p->topk > 4096)
+      return DSA_ERR_UNSUPPORTED;
+    *path = kPathF32;
+    return DSA_OK;
+  }
+  if ((it == DSA_BF16 || it == DSA_FP8_E4M3) && at == DSA_BF16 && (ot == DSA_BF16 || ot == DSA_F32)) {
+    if (!is_v32_dims_index(*p) || !is_v32_dims_attn(*p)) return DSA_ERR_UNSUPPORTED;
+    *path = it == DSA_BF16 ? kPathBF16 : kPathFP8;
+    return DSA_OK;
+  }
+  return DSA_ERR_UNSUPPORTED;
+}
+
+dsa_status_t hip_status(hipError_t e) { return e == hipSuccess ? DSA_OK : DSA_ERR_HIP; }
+
+int chunk_queries(const dsa_problem_t& p) {
+  const int64_t row_bytes = (int64_t)p.kv_len * 4 * p.batch;
+  int64_t cq = (int64_t)kScoresBudget / row_bytes;
+  if (cq >= p.q_len) return p.q_len;
+  if (cq >= 8) cq = cq / 8 * 8;
+  return (int)(cq < 1 ? 1 : cq);
+}
+
+int attn_splits(const dsa_problem_t& p, Path path, int rows) {
+  return path == kPathF32 ? 1 : attn_splits_bf16(rows, p.topk);
+}
+
+size_t attn_partials_bytes(const dsa_problem_t& p, int rows, int splits) {
+  if (splits <= 1) return 0;
+  return align_up((size_t)rows * splits * p.attn_heads * p.v_dim * 4) +
+         align_up((size_t)rows * splits * p.attn_heads * 4);
+}
+
+struct ForwardPlan {
+  int chunk;       // queries per chunk
+  int n_chunks;
+  size_t scores_bytes, idx_bytes, part_bytes;
+};
+
+ForwardPlan plan_forward(const dsa_problem_t& p, Path path, bool need_idx) {
+  ForwardPlan f;
+  f.chunk = chunk_queries(p);
+  f.n_chunks = (p.q_len + f.chunk - 1) / f.chunk;
+  f.scores_bytes = align_up((size_t)p.batch * f.chunk * p.kv_len * 4);
+  f.idx_bytes = need_idx ? align_up((size_t)p.batch * p.q_len * p.topk * 4) : 0;
+  const int rows = p.batch * f.chunk;
+  f.part_bytes = attn_partials_bytes(p, rows, attn_splits(p, path, rows));
+  return f;
+}
+
+IndexLaunch make_index(const dsa_problem_t& p, const void* q, const uint8_t* qs, const void* k, const uint8_t* ks,
+                       const float* w, float* scores, int64_t row_stride, int q_begin, int q_count, int masked) {
+  IndexLaunch a;
+  a.q = q; a.q_scale = qs; a.k = k; a.k_scale = ks; a.w = w;
+  a.scores = scores; a.row_stride = row_stride;
+  a.B = p.batch; a.Lq = p.q_len; a.Lk = p.kv_len; a.H = p.index_heads; a.D = p.index_dim;
+  a.q_begin = q_begin; a.q_count = q_count; a.write_masked = masked;
+  return a;
+}
+
+TopkLaunch make_topk(const dsa_problem_t& p, const float* scores, int64_t row_stride, int32_t* out,
+                     int q_begin, int q_count) {
+  TopkLaunch a;
+  a.scores = scores; a.row_stride = row_stride; a.out = out;
+  a.B = p.batch; a.Lq = p.q_len; a.Lk = p.kv_len; a.K = p.topk;
+  a.q_begin = q_begin; a.q_count = q_count;
+  a.vec_ok = aligned16(scores) && (row_stride % 4) == 0;
+  return a;
+}
+
+AttnLaunch make_attn(const dsa_problem_t& p, const void* qa, const void* kv, const int32_t* idx, void* out,
+                     float* lse, int q_begin, int q_count, int splits, void* part) {
+  AttnLaunch a;
+  a.qa = qa; a.kv = kv; a.idx = idx; a.out = out; a.lse = lse;
+  a.B = p.batch; a.Lq = p.q_len; a.Lk = p.kv_len; a.NH = p.attn_heads; a.Dqk = p.qk_dim; a.Dv = p.v_dim;
+  a.K = p.topk; a.q_begin = q_begin; a.q_count = q_count; a.splits = splits;
+  a.scale = p.softmax_scale; a.out_f32 = p.out_dtype == DSA_F32;
+  a.part_o = nullptr; a.part_lse = nullptr;
+  if (splits > 1) {
+    const int rows = p.batch * q_count;
+    a.part_o = static_cast<float*>(part);
+    a.part_lse = reinterpret_cast<float*>(static_cast<char*>(part) +
+                                          align_up((size_t)rows * splits * p.attn_heads * p.v_dim * 4));
+  }
+  return a;
+}
+
+hipError_t run_index(Path path, const IndexLaunch& a, hipStream_t s) {
+  if (path == kPathF32) return launch_index_f32(a, s);
+  if (path == kPathBF16) return launch_index_bf16(a, s);
+  return launch_index_fp8(a, s);
+}
+
+dsa_status_t check_index_ptrs(Path path, const void* q, const uint8_t* qs, const void* k, const uint8_t* ks,
+                              const float* w) {
+  if (!q || !k || !w) return DSA_ERR_INVALID_ARGUMENT;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(w)) return DSA_ERR_INVALID_ARGUMENT;
+  if (path == kPathFP8 && (!qs || !ks)) return DSA_ERR_INVALID_ARGUMENT;
+  return DSA_OK;
+}
+
+dsa_status_t check_attn_ptrs(const void* qa, const void* kv, const void* out) {
+  if (!qa || !kv || !out) return DSA_ERR_INVALID_ARGUMENT;
+  if (!aligned16(qa) || !aligned16(kv) || !aligned16(out)) return DSA_ERR_INVALID_ARGUMENT;
+  return DSA_OK;
+}
+
+// Records events[slot*2 + which] if that slot exists.
+struct EventSink {
+  hipEvent_t* ev;
+  int n_slots;
+  hipStream_t s;
+  hipError_t rec(int chunk, int stage, int which) const {
+    const int slot = chunk * DSA_NUM_STAGES + stage;
+    if (!ev || slot >= n_slots) return hipSuccess;
+    return hipEventRecord(ev[2 * slot + which], s);
+  }
+};
+
+dsa_status_t forward_impl(const dsa_problem_t* prob, const void* q_idx, const uint8_t* q_scale, const void* k_idx,
+                          const uint8_t* k_scale, const float* head_w, const void* q_attn, const void* kv,
+                          int32_t* topk_idx, void* out, float* lse, void* workspace, size_t workspace_bytes,
+                          const EventSink& ev, int32_t* n_chunks_out, hipStream_t stream) {
+  Path path;
+  dsa_status_t st = check_problem(prob, &path);
+  if (st != DSA_OK) return st;
+  const dsa_problem_t& p = *prob;
+  if ((st = check_index_ptrs(path, q_idx, q_scale, k_idx, k_scale, head_w)) != DSA_OK) return st;
+  if ((st = check_attn_ptrs(q_attn, kv, out)) != DSA_OK) return st;
+  if ((topk_idx && !aligned16(topk_idx)) || (lse && !aligned16(lse))) return DSA_ERR_INVALID_ARGUMENT;
+  const ForwardPlan f = plan_forward(p, path, topk_idx == nullptr);
+  const size_t need = f.scores_bytes + f.idx_bytes + f.part_bytes;
+  if (workspace_bytes < need) return DSA_ERR_WORKSPACE_TOO_SMALL;
+  if (!workspace || !aligned16(workspace)) return DSA_ERR_INVALID_ARGUMENT;
+  if (n_chunks_out) *n_chunks_out = f.n_chunks;
+
+  char* ws = static_cast<char*>(workspace);
+  float* scores = reinterpret_cast<float*>(ws);
+  int32_t* idx = topk_idx ? topk_idx : reinterpret_cast<int32_t*>(ws + f.scores_bytes);
+  void* part = ws + f.scores_bytes + f.idx_bytes;
+
+  for (int c = 0; c < f.n_chunks; ++c) {
+    const int q0 = c * f.chunk;
+    const int qn = p.q_len - q0 < f.chunk ? p.q_len - q0 : f.chunk;
+    hipError_t e;
+    // 1. scores for this chunk's rows (causal part only)
+    if ((e = ev.rec(c, 0, 0)) != hipSuccess) return DSA_ERR_HIP;
+    IndexLaunch ia = make_index(p, q_idx, q_scale, k_idx, k_scale, head_w, scores, p.kv_len, q0, qn, 0);
+    if ((e = run_index(path, ia, stream)) != hipSuccess) return hip_status(e);
+    if ((e = ev.rec(c, 0, 1)) != hipSuccess) return DSA_ERR_HIP;
+    // 2. top-k
+    if ((e = ev.rec(c, 1, 0)) != hipSuccess) return DSA_ERR_HIP;
+    if ((e = launch_topk(make_topk(p, scores, p.kv_len, idx, q0, qn), stream)) != hipSuccess) return hip_status(e);
+    if ((e = ev.rec(c, 1, 1)) != hipSuccess) return DSA_ERR_HIP;
+    // 3. attention (+ combine); every chunk uses the split count the
+    //    workspace was sized for (that of a full chunk)
+    const int splits = attn_splits(p, path, p.batch * f.chunk);
+    AttnLaunch aa = make_attn(p, q_attn, kv, idx, out, lse, q0, qn, splits, part);
+    if ((e = ev.rec(c, 2, 0)) != hipSuccess) return DSA_ERR_HIP;
+    e = path == kPathF32 ? launch_attn_f32(aa, stream) : launch_attn_bf16(aa, stream);
+    if (e != hipSuccess) return hip_status(e);
+    if ((e = ev.rec(c, 2, 1)) != hipSuccess) return DSA_ERR_HIP;
+    if ((e = ev.rec(c, 3, 0)) != hipSuccess) return DSA_ERR_HIP;
+    if (splits > 1 && (e = launch_attn_combine(aa, stream)) != hipSuccess) return hip_status(e);
+    if ((e = ev.rec(c, 3, 1)) != hipSuccess) return DSA_ERR_HIP;
+  }
+  return DSA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+dsa_status_t dsa_index_scores(const dsa_problem_t* prob, const void* q_idx, const uint8_t* q_scale,
+                              const void* k_idx, const uint8_t* k_scale, const float* head_w, float* scores,
+                              hipStream_t stream) {
+  Path path;
+  dsa_status_t st = check_problem(prob, &path);
+  if (st != DSA_OK) return st;
+  if ((st = check_index_ptrs(path, q_idx, q_scale, k_idx, k_scale, head_w)) != DSA_OK) return st;
+  if (!scores || !aligned16(scores)) return DSA_ERR_INVALID_ARGUMENT;
+  const dsa_problem_t& p = *prob;
+  IndexLaunch a = make_index(p, q_idx, q_scale, k_idx, k_scale, head_w, scores, p.kv_len, 0, p.q_len, 1);
+  return hip_status(run_index(path, a, stream));
+}
+
+dsa_status_t dsa_topk(const dsa_problem_t* prob, const float* scores, int64_t row_stride, int32_t* topk_idx,
+                      hipStream_t stream) {
+  Path path;
+  dsa_status_t st = check_problem(prob, &path);
+  if (st != DSA_OK) return st;
+  if (!scores || !topk_idx || row_stride < prob->kv_len) return DSA_ERR_INVALID_ARGUMENT;
+  if ((reinterpret_cast<uintptr_t>(scores) & 3u) || (reinterpret_cast<uintptr_t>(topk_idx) & 3u))
+    return DSA_ERR_INVALID_ARGUMENT;
+  return hip_status(launch_topk(make_topk(*prob, scores, row_stride, topk_idx, 0, prob->q_len), stream));
+}
+
+dsa_status_t dsa_sparse_mla_attn(const dsa_problem_t* prob, const void* q_attn, const void* kv,
+                                 const int32_t* topk_idx, void* out, float* lse, void* workspace,
+                                 size_t workspace_bytes, hipStream_t stream) {
+  Path path;
+  dsa_status_t st = check_problem(prob, &path);
+  if (st != DSA_OK) return st;
+  if ((st = check_attn_ptrs(q_attn, kv, out)) != DSA_OK) return st;
+  if (!topk_idx || !aligned16(topk_idx) || (lse && !aligned16(lse))) return DSA_ERR_INVALID_ARGUMENT;
+  const dsa_problem_t& p = *prob;
+  const int rows = p.batch * p.q_len;
+  const int splits = attn_splits(p, path, rows);
+  const size_t need = attn_partials_bytes(p, rows, splits);
+  if (workspace_bytes < need) return DSA_ERR_WORKSPACE_TOO_SMALL;
+  if (need > 0 && (!workspace || !aligned16(workspace))) return DSA_ERR_INVALID_ARGUMENT;
+  AttnLaunch a = make_attn(p, q_attn, kv, topk_idx, out, lse, 0, p.q_len, splits, workspace);
+  hipError_t e = path == kPathF32 ? launch_attn_f32(a, stream) : launch_attn_bf16(a, stream);
+  if (e != hipSuccess) return hip_status(e);
+  if (splits > 1) return hip_status(launch_attn_combine(a, stream));
+  return DSA_OK;
+}
+
+dsa_status_t dsa_forward(const dsa_problem_t* prob, const void* q_idx, const uint8_t* q_scale, const void* k_idx,
+                         const uint8_t* k_scale, const float* head_w, const void* q_attn, const void* kv,
+                         int32_t* topk_idx, void* out, float* lse, void* workspace, size_t workspace_bytes,
+                         hipStream_t stream) {
+  EventSink none{nullptr, 0, stream};
+  return forward_impl(prob, q_idx, q_scale, k_idx, k_scale, head_w, q_attn, kv, topk_idx, out, lse, workspace,
+                      workspace_bytes, none, nullptr, stream);
+}
+
+dsa_status_t dsa_forward_timed(const dsa_problem_t* prob, const void* q_idx, const uint8_t* q_scale,
+                               const void* k_idx, const uint8_t* k_scale, const float* head_w, const void* q_attn,
+                               const void* kv, int32_t* topk_idx, void* out, float* lse, void* workspace,
+                               size_t workspace_bytes, hipEvent_t* events, int32_t n_event_slots,
+                               int32_t* n_chunks_out, hipStream_t stream) {
+  if (n_event_slots < 0 || (n_event_slots > 0 && !events)) return DSA_ERR_INVALID_ARGUMENT;
+  EventSink sink{events, n_event_slots / 2, stream};
+  return forward_impl(prob, q_idx, q_scale, k_idx, k_scale, head_w, q_attn, kv, topk_idx, out, lse, workspace,
+                      workspace_bytes, sink, n_chunks_out, stream);
+}
+
+size_t dsa_workspace_size(const dsa_problem_t* prob, int32_t op) {
+  Path path;
+  if (check_problem(prob, &path) != DSA_OK) return 0;
+  const dsa_problem_t& p = *prob;
+  if (op == DSA_OP_ATTN) {
+    const int rows = p.batch * p.q_len;
+    return attn_partials_bytes(p, rows, attn_splits(p, path, rows));
+  }
+  if (op == DSA_OP_FORWARD) {
+    const ForwardPlan f = plan_forward(p, path, true);
+    return f.scores_bytes + f.idx_bytes + f.part_bytes;
+  }
+  return 0;
+}
+
+int32_t dsa_forward_chunks(const dsa_problem_t* prob) {
+  Path path;
+  if (check_problem(prob, &path) != DSA_OK) return 0;
+  return plan_forward(*prob, path, true).n_chunks;
+}
+
+const char* dsa_status_string(dsa_status_t s) {
+  switch (s) {
+    case DSA_OK: return "ok";
+    case DSA_ERR_INVALID_ARGUMENT: return "invalid argument";
+    case DSA_ERR_UNSUPPORTED: return "unsupported problem (dtype combination or dims)";
+    case DSA_ERR_WORKSPACE_TOO_SMALL: return "workspace too small";
+    case DSA_ERR_HIP: return "HIP runtime or launch error";
+  }
+  return "unknown status";
+}
+
+int32_t dsa_abi_version(void) { return DSA_ABI_VERSION; }
+
+}  // extern "C"

@@ -1,0 +1,65 @@
+// Internal launch interface between the C-ABI front end (dsa_api.cpp) and
+// the kernel translation units.  Host-only declarations.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <stddef.h>
+
+namespace dsa {
+
+// Which queries of each sequence a launch covers: [q_begin, q_begin + q_count).
+// Score rows and top-k rows of a launch are numbered r = b * q_count + (i - q_begin).
+struct IndexLaunch {
+  const void* q;           // [B][Lq][H][D] (bf16, f32 or fp8 codes)
+  const uint8_t* q_scale;  // [B][Lq][H] ue8m0, fp8 only
+  const void* k;           // [B][Lk][D]
+  const uint8_t* k_scale;  // [B][Lk] ue8m0, fp8 only
+  const float* w;          // [B][Lq][H]
+  float* scores;           // rows of row_stride floats
+  int64_t row_stride;
+  int B, Lq, Lk, H, D;
+  int q_begin, q_count;
+  int write_masked;        // also write -inf for positions beyond the causal limit
+};
+
+struct TopkLaunch {
+  const float* scores;     // rows as above
+  int64_t row_stride;
+  int32_t* out;            // row r at out + (b*Lq + i) * K  (full-tensor numbering)
+  int B, Lq, Lk, K;
+  int q_begin, q_count;
+  int vec_ok;              // rows are 16-byte aligned: use 16-byte loads
+};
+
+struct AttnLaunch {
+  const void* qa;          // [B][Lq][NH][Dqk]
+  const void* kv;          // [B][Lk][Dqk]
+  const int32_t* idx;      // [B][Lq][K] (full-tensor numbering)
+  void* out;               // [B][Lq][NH][Dv]
+  float* lse;              // [B][Lq][NH] or null
+  float* part_o;           // split partials [rows][S][NH][Dv] fp32 (S > 1 only)
+  float* part_lse;         // [rows][S][NH]
+  int B, Lq, Lk, NH, Dqk, Dv, K;
+  int q_begin, q_count;
+  int splits;              // S: key ranges per query (1 = no combine step)
+  float scale;
+  int out_f32;             // out dtype: 1 fp32, 0 bf16
+};
+
+// Indexer.  *_bf16 / *_fp8 need H = 64, D = 128.
+hipError_t launch_index_f32(const IndexLaunch& a, hipStream_t s);
+hipError_t launch_index_bf16(const IndexLaunch& a, hipStream_t s);
+hipError_t launch_index_fp8(const IndexLaunch& a, hipStream_t s);
+
+// Top-k (all dtypes: scores are fp32).
+hipError_t launch_topk(const TopkLaunch& a, hipStream_t s);
+
+// Sparse MLA.  *_bf16 needs NH = 128, Dqk = 576, Dv = 512.
+hipError_t launch_attn_f32(const AttnLaunch& a, hipStream_t s);
+hipError_t launch_attn_bf16(const AttnLaunch& a, hipStream_t s);
+hipError_t launch_attn_combine(const AttnLaunch& a, hipStream_t s);
+
+// Split count the bf16 attention uses for a launch of `rows` queries.
+int attn_splits_bf16(int rows, int K);
+
+}  // namespace dsa

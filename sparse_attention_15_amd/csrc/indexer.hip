@@ -1,0 +1,340 @@
+// Lightning-indexer scores on gfx950.
+//
+// For query (b, i) at position p and key s <= p:
+//     I[s] = sum_h w[h] * max(0, q_h . k_s)
+// (HF model doc "DeepSeek-V3.2", section "DeepSeek Sparse Attention (DSA)",
+// item 1: a scorer with few heads rates every earlier key; the index keys are
+// one head of index_head_dim per token; per-query head weights come from the
+// indexer's weights_proj.  The ReLU-gated, weighted head sum is the reading
+// this library implements.)
+//
+// bf16 / fp8 kernels (H = 64, D = 128): the per-head dot products are an MFMA
+// GEMM with heads on the M axis (4 tiles of 16) and keys on the N axis, so
+// the ReLU-weighted head reduction happens in registers: 16 values per lane,
+// then two cross-lane adds.  Keys are read once per query group: straight
+// from HBM into registers for decode-shaped launches, through a swizzled,
+// double-buffered LDS tile shared by 8 queries for prefill-shaped ones.
+// FP8 (E4M3 codes + ue8m0 row scales): the MFMA consumes raw codes; the
+// query-row scales fold into the head weights and the key scale multiplies
+// the head sum.  Both are powers of two and ReLU is positively homogeneous,
+// so this equals scoring the dequantised values.
+#include "dsa_device.h"
+#include "dsa_internal.h"
+
+namespace dsa {
+namespace {
+
+constexpr float kNegInf = -__builtin_inff();
+
+// ------------------------------------------------------------- fp32 -------
+// One thread per key; the query's H x D block and head weights sit in LDS.
+__global__ __launch_bounds__(256) void idx_f32_kernel(IndexLaunch a) {
+  extern __shared__ float sm[];
+  const int H = a.H, D = a.D;
+  float* qs = sm;
+  float* ws = sm + H * D;
+  const int row = blockIdx.y;
+  const int b = row / a.q_count;
+  const int i = a.q_begin + row % a.q_count;
+  const int n = a.Lk - a.Lq + i + 1;
+  const int s0 = blockIdx.x * 256;
+  if (s0 >= n && !a.write_masked) return;
+  const int64_t qrow = (int64_t)b * a.Lq + i;
+  const float* qg = static_cast<const float*>(a.q) + qrow * H * D;
+  for (int e = threadIdx.x; e < H * D; e += 256) qs[e] = qg[e];
+  for (int e = threadIdx.x; e < H; e += 256) ws[e] = a.w[qrow * H + e];
+  __syncthreads();
+  const int s = s0 + threadIdx.x;
+  if (s >= a.Lk) return;
+  float* out = a.scores + (int64_t)row * a.row_stride;
+  if (s >= n) {
+    if (a.write_masked) out[s] = kNegInf;
+    return;
+  }
+  const float* kr = static_cast<const float*>(a.k) + ((int64_t)b * a.Lk + s) * D;
+  float acc = 0.f;
+  for (int h = 0; h < H; ++h) {
+    float x = 0.f;
+    for (int d = 0; d < D; ++d) x = fmaf(qs[h * D + d], kr[d], x);
+    acc = fmaf(ws[h], fmaxf(x, 0.f), acc);
+  }
+  out[s] = acc;
+}
+
+// -------------------------------------------------- MFMA building blocks ---
+// Lane l of a wave works on column r = l % 16 of a 16-wide key tile and on
+// k-group g = l / 16.  bf16: k-step t (0..3) covers dims 32t + 8g .. +8.
+// fp8: one 16x16x128 MFMA covers all 128 dims; group g holds dims 32g .. +32.
+constexpr int kH = 64;
+constexpr int kD = 128;
+
+template <bool FP8> struct QFrag;
+template <> struct QFrag<false> { u32x4 v[4][4]; };  // [m-tile][k-step]
+template <> struct QFrag<true>  { i32x8 v[4]; };     // [m-tile]
+template <bool FP8> struct KFrag;
+template <> struct KFrag<false> { u32x4 v[4]; };     // [k-step]
+template <> struct KFrag<true>  { i32x8 v; };
+
+__device__ __forceinline__ i32x8 join(u32x4 lo, u32x4 hi) {
+  i32x8 r;
+  r[0] = lo[0]; r[1] = lo[1]; r[2] = lo[2]; r[3] = lo[3];
+  r[4] = hi[0]; r[5] = hi[1]; r[6] = hi[2]; r[7] = hi[3];
+  return r;
+}
+
+// Query fragments and the 16 head weights this lane needs (heads 16m + 4g + j).
+template <bool FP8>
+__device__ __forceinline__ void load_query(const IndexLaunch& a, int64_t qrow, int lane,
+                                           QFrag<FP8>& q, float (&wv)[16]) {
+  const int r = lane & 15, g = lane >> 4;
+  if constexpr (!FP8) {
+    const uint8_t* base = static_cast<const uint8_t*>(a.q) + qrow * (kH * kD * 2);
+#pragma unroll
+    for (int m = 0; m < 4; ++m)
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+        q.v[m][t] = ld16(base + ((16 * m + r) * kD + 32 * t + 8 * g) * 2);
+  } else {
+    const uint8_t* base = static_cast<const uint8_t*>(a.q) + qrow * (kH * kD);
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      const uint8_t* p = base + (16 * m + r) * kD + 32 * g;
+      q.v[m] = join(ld16(p), ld16(p + 16));
+    }
+  }
+  const float* w = a.w + qrow * kH;
+#pragma unroll
+  for (int m = 0; m < 4; ++m)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int h = 16 * m + 4 * g + j;
+      float wh = w[h];
+      if constexpr (FP8) wh *= ue8m0_to_f32(a.q_scale[qrow * kH + h]);
+      wv[4 * m + j] = wh;
+    }
+}
+
+// Key fragments of the 16-key tile starting at key k0 (rows past the end are
+// clamped to the last row; their scores are never stored).
+template <bool FP8>
+__device__ __forceinline__ void load_keys_global(const uint8_t* kbase, int k0, int Lk, int lane, KFrag<FP8>& kf) {
+  const int r = lane & 15, g = lane >> 4;
+  const int key = min(k0 + r, Lk - 1);
+  if constexpr (!FP8) {
+    const uint8_t* p = kbase + (int64_t)key * (kD * 2) + 16 * g;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) kf.v[t] = ld16_stream(p + 64 * t);
+  } else {
+    const uint8_t* p = kbase + (int64_t)key * kD + 32 * g;
+    kf.v = join(ld16_stream(p), ld16_stream(p + 16));
+  }
+}
+
+// Scores of one 16-key tile for one query: returns the score of key r in
+// every lane (all four k-groups hold the same value after the reduction).
+template <bool FP8>
+__device__ __forceinline__ float tile_score(const QFrag<FP8>& q, const KFrag<FP8>& kf, const float (&wv)[16]) {
+  f32x4 acc[4];
+#pragma unroll
+  for (int m = 0; m < 4; ++m) acc[m] = f32x4{0.f, 0.f, 0.f, 0.f};
+  if constexpr (!FP8) {
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+      for (int m = 0; m < 4; ++m) acc[m] = mfma16(q.v[m][t], kf.v[t], acc[m]);
+  } else {
+#pragma unroll
+    for (int m = 0; m < 4; ++m)
+      acc[m] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(q.v[m], kf.v, acc[m], 0, 0, 0, 127, 0, 127);
+  }
+  float s = 0.f;
+#pragma unroll
+  for (int m = 0; m < 4; ++m)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) s = fmaf(wv[4 * m + j], fmaxf(acc[m][j], 0.f), s);
+  s += shfl_xor(s, 16);
+  s += shfl_xor(s, 32);
+  return s;
+}
+
+// ------------------------------------------------------ decode shape -------
+// grid (ceil(Lk / chunk), B * q_count), 4 waves; wave w streams keys
+// [c0 + w*chunk/4, c0 + (w+1)*chunk/4) of its query in 64-key steps, with
+// the next step's loads in flight while the current step computes.
+template <bool FP8>
+__global__ __launch_bounds__(256, 2) void idx_decode_kernel(IndexLaunch a, int chunk) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int row = blockIdx.y;
+  const int b = row / a.q_count;
+  const int i = a.q_begin + row % a.q_count;
+  const int n = a.Lk - a.Lq + i + 1;
+  const int per_wave = chunk >> 2;
+  const int w0 = blockIdx.x * chunk + wave * per_wave;
+  const int w1 = min(w0 + per_wave, a.Lk);
+  const int wn = min(w1, n);
+  float* out = a.scores + (int64_t)row * a.row_stride;
+  if (a.write_masked)
+    for (int s = max(w0, n) + lane; s < w1; s += 64) out[s] = kNegInf;
+  if (w0 >= wn) return;
+
+  const int64_t qrow = (int64_t)b * a.Lq + i;
+  QFrag<FP8> q;
+  float wv[16];
+  load_query<FP8>(a, qrow, lane, q, wv);
+  const uint8_t* kbase = static_cast<const uint8_t*>(a.k) + (int64_t)b * a.Lk * (FP8 ? kD : 2 * kD);
+  const uint8_t* ks = FP8 ? a.k_scale + (int64_t)b * a.Lk : nullptr;
+
+  KFrag<FP8> cur[4], nxt[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) load_keys_global<FP8>(kbase, w0 + 16 * j, a.Lk, lane, cur[j]);
+  for (int k0 = w0; k0 < wn; k0 += 64) {
+    const bool more = k0 + 64 < wn;
+    if (more) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) load_keys_global<FP8>(kbase, k0 + 64 + 16 * j, a.Lk, lane, nxt[j]);
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      float s = tile_score<FP8>(q, cur[j], wv);
+      const int key = k0 + 16 * j + lane;
+      if constexpr (FP8) {
+        if (lane < 16 && key < wn) s *= ue8m0_to_f32(ks[key]);
+      }
+      if (lane < 16 && key < wn) out[key] = s;
+    }
+    if (more) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) cur[j] = nxt[j];
+    }
+  }
+}
+
+// ----------------------------------------------------- prefill shape -------
+// grid (ceil(q_count / QB), ksplit, B), QB waves = QB consecutive queries.
+// The block walks 64-key tiles kt = blockIdx.y, +ksplit, ... up to the last
+// query's causal limit; each tile is staged once in LDS (16-byte chunks
+// XOR-swizzled by row so the MFMA operand reads are bank-conflict free) and
+// consumed by all QB waves.
+template <bool FP8, int QB>
+__global__ __launch_bounds__(QB * 64) void idx_prefill_kernel(IndexLaunch a, int ksplit) {
+  constexpr int TK = 64;
+  constexpr int ROWB = FP8 ? kD : 2 * kD;        // bytes per key row
+  constexpr int CPR = ROWB / 16;                  // 16-byte chunks per row
+  constexpr int NT = QB * 64;
+  constexpr int CPT = TK * CPR / NT;              // chunks per thread per tile
+  static_assert(CPT >= 1 && TK * CPR % NT == 0, "tile/threads mismatch");
+  __shared__ __attribute__((aligned(16))) uint8_t lds[2][TK * ROWB];
+
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int qb = gridDim.x - 1 - blockIdx.x;      // longest rows first
+  const int b = blockIdx.z;
+  const int ii = qb * QB + wave;
+  const bool active = ii < a.q_count;
+  const int i = a.q_begin + ii;
+  const int p = a.Lk - a.Lq + i;
+  const int last = min(qb * QB + QB, a.q_count) - 1;
+  const int n_max = a.Lk - a.Lq + a.q_begin + last + 1;
+  const int ntiles = (n_max + TK - 1) / TK;
+  const int row = b * a.q_count + ii;
+  float* out = a.scores + (int64_t)row * a.row_stride;
+
+  QFrag<FP8> q;
+  float wv[16];
+  if (active) load_query<FP8>(a, (int64_t)b * a.Lq + i, lane, q, wv);
+  const uint8_t* kbase = static_cast<const uint8_t*>(a.k) + (int64_t)b * a.Lk * ROWB;
+  const uint8_t* ks = FP8 ? a.k_scale + (int64_t)b * a.Lk : nullptr;
+
+  u32x4 stage[CPT];
+  auto gload = [&](int kt) {
+#pragma unroll
+    for (int c = 0; c < CPT; ++c) {
+      const int cid = threadIdx.x + c * NT;
+      const int r = cid / CPR, ch = cid % CPR;
+      const int key = min(kt * TK + r, a.Lk - 1);
+      stage[c] = ld16(kbase + (int64_t)key * ROWB + ch * 16);
+    }
+  };
+  auto lstore = [&](int buf) {
+#pragma unroll
+    for (int c = 0; c < CPT; ++c) {
+      const int cid = threadIdx.x + c * NT;
+      const int r = cid / CPR, ch = cid % CPR;
+      st16(&lds[buf][r * ROWB + ((ch ^ (r & (CPR - 1))) * 16)], stage[c]);
+    }
+  };
+
+  const int r16 = lane & 15, g = lane >> 4;
+  int kt = blockIdx.y;
+  int buf = 0;
+  if (kt < ntiles) {
+    gload(kt);
+    lstore(0);
+  }
+  __syncthreads();
+  for (; kt < ntiles; kt += ksplit) {
+    const int nk = kt + ksplit;
+    if (nk < ntiles) gload(nk);
+    if (active && kt * TK <= p) {
+#pragma unroll
+      for (int j = 0; j < TK / 16; ++j) {
+        const int rr = 16 * j + r16;
+        const uint8_t* lrow = &lds[buf][rr * ROWB];
+        KFrag<FP8> kf;
+        if constexpr (!FP8) {
+#pragma unroll
+          for (int t = 0; t < 4; ++t) kf.v[t] = ld16(lrow + (((4 * t + g) ^ (rr & 15)) * 16));
+        } else {
+          kf.v = join(ld16(lrow + (((2 * g) ^ (rr & 7)) * 16)), ld16(lrow + (((2 * g + 1) ^ (rr & 7)) * 16)));
+        }
+        float s = tile_score<FP8>(q, kf, wv);
+        const int key = kt * TK + 16 * j + lane;
+        if (lane < 16 && key <= p) {
+          if constexpr (FP8) s *= ue8m0_to_f32(ks[key]);
+          out[key] = s;
+        }
+      }
+    }
+    if (nk < ntiles) lstore(buf ^ 1);
+    __syncthreads();
+    buf ^= 1;
+  }
+  if (a.write_masked && active && blockIdx.y == 0)
+    for (int s = p + 1 + lane; s < a.Lk; s += 64) out[s] = kNegInf;
+}
+
+int pick_ksplit(int blocks, int ntiles_max) {
+  int ks = 1;
+  while (blocks * ks < 1024 && ks * 8 <= ntiles_max) ks *= 2;
+  return ks;
+}
+
+template <bool FP8>
+hipError_t launch_mfma(const IndexLaunch& a, hipStream_t s) {
+  if (a.q_count <= 4) {
+    const int chunk = 2048;
+    dim3 grid((a.Lk + chunk - 1) / chunk, a.B * a.q_count);
+    hipLaunchKernelGGL(idx_decode_kernel<FP8>, grid, dim3(256), 0, s, a, chunk);
+  } else {
+    constexpr int QB = 8;
+    const int nqb = (a.q_count + QB - 1) / QB;
+    const int n_max = a.Lk - a.Lq + a.q_begin + a.q_count;
+    const int ks = pick_ksplit(nqb * a.B, (n_max + 63) / 64);
+    dim3 grid(nqb, ks, a.B);
+    hipLaunchKernelGGL((idx_prefill_kernel<FP8, QB>), grid, dim3(QB * 64), 0, s, a, ks);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_index_f32(const IndexLaunch& a, hipStream_t s) {
+  dim3 grid((a.Lk + 255) / 256, a.B * a.q_count);
+  const size_t smem = (size_t)(a.H * a.D + a.H) * sizeof(float);
+  hipLaunchKernelGGL(idx_f32_kernel, grid, dim3(256), smem, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_index_bf16(const IndexLaunch& a, hipStream_t s) { return launch_mfma<false>(a, s); }
+hipError_t launch_index_fp8(const IndexLaunch& a, hipStream_t s) { return launch_mfma<true>(a, s); }
+
+}  // namespace dsa

@@ -1,0 +1,106 @@
+"""C-ABI checks that need no GPU: the library loads, exports every symbol the
+header declares, and rejects bad arguments before touching the HIP runtime."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from dsa_workloads import configs as C
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "dsa.h")
+LIB = os.path.join(ROOT, "sparse_attention_15_amd", "libdsa.so")
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:dsa_status_t|size_t|int32_t|const char\*)\s+(dsa_\w+)\s*\(", text, re.M)))
+
+
+@pytest.fixture(scope="module")
+def dsa():
+    if not os.path.exists(LIB):
+        pytest.fail("libdsa.so is not built (run __graft_entry__.build())")
+    import sparse_attention_15_amd.dsa as d
+    return d
+
+
+def test_header_declares_the_boundary():
+    names = _declared_functions()
+    for required in ("dsa_index_scores", "dsa_topk", "dsa_sparse_mla_attn", "dsa_forward",
+                     "dsa_workspace_size", "dsa_status_string", "dsa_abi_version"):
+        assert required in names
+
+
+def test_library_exports_every_declared_symbol(dsa):
+    L = dsa.lib()
+    for name in _declared_functions():
+        assert hasattr(L, name), name
+    assert dsa.abi_version() == 1
+
+
+def test_status_strings(dsa):
+    for s in range(5):
+        assert dsa.status_string(s)
+
+
+def _prob(dsa, cfg, **kw):
+    p = dsa.make_problem(cfg)
+    for k, v in kw.items():
+        setattr(p, k, v)
+    return p
+
+
+def test_workspace_size_is_host_only_and_sane(dsa):
+    p = dsa.make_problem(C.DECODE_32K)
+    ws = dsa.workspace_size(p, dsa.DSA_OP_FORWARD)
+    assert ws >= 32 * 32768 * 4 + 32 * 2048 * 4
+    assert dsa.workspace_size(p, 99) == 0
+    bad = _prob(dsa, C.DECODE_32K, q_len=0)
+    assert dsa.workspace_size(bad, dsa.DSA_OP_FORWARD) == 0
+    p5 = dsa.make_problem(C.PREFILL_64K_FP8)
+    assert dsa.forward_chunks(p5) > 1          # 16 GiB of scores are never materialised at once
+    assert dsa.forward_chunks(dsa.make_problem(C.PREFILL_8K)) == 1
+
+
+def _call_forward(dsa, p, ptr=16, ws_bytes=1 << 40, q_scale=None):
+    L = dsa.lib()
+    v = ctypes.c_void_p(ptr)
+    return L.dsa_forward(ctypes.byref(p), v, q_scale, v, q_scale, v, v, v, None, v, None, v, ws_bytes, None)
+
+
+def test_invalid_arguments_are_rejected_before_launch(dsa):
+    L = dsa.lib()
+    p = dsa.make_problem(C.DECODE_32K)
+    # null pointers
+    assert _call_forward(dsa, p, ptr=0) == dsa.DSA_ERR_INVALID_ARGUMENT
+    # misaligned pointer
+    assert _call_forward(dsa, p, ptr=24) == dsa.DSA_ERR_INVALID_ARGUMENT
+    # workspace too small
+    assert _call_forward(dsa, p, ws_bytes=16) == dsa.DSA_ERR_WORKSPACE_TOO_SMALL
+    # bad dims
+    for field, val in (("q_len", 0), ("kv_len", 0), ("topk", 0), ("batch", -1), ("v_dim", 1000)):
+        bad = _prob(dsa, C.DECODE_32K, **{field: val})
+        assert _call_forward(dsa, bad) == dsa.DSA_ERR_INVALID_ARGUMENT, field
+    # q_len > kv_len
+    assert _call_forward(dsa, _prob(dsa, C.DECODE_32K, q_len=40000)) == dsa.DSA_ERR_INVALID_ARGUMENT
+    # non-finite scale
+    assert _call_forward(dsa, _prob(dsa, C.DECODE_32K, softmax_scale=float("nan"))) == dsa.DSA_ERR_INVALID_ARGUMENT
+    # unsupported: bf16 with non-V3.2 dims, mixed f32/bf16
+    assert _call_forward(dsa, _prob(dsa, C.DECODE_32K, index_heads=32)) == dsa.DSA_ERR_UNSUPPORTED
+    assert _call_forward(dsa, _prob(dsa, C.DECODE_32K, index_dtype=dsa.DSA_F32)) == dsa.DSA_ERR_UNSUPPORTED
+    # fp8 without scales
+    p8 = dsa.make_problem(C.PREFILL_64K_FP8)
+    assert _call_forward(dsa, p8) == dsa.DSA_ERR_INVALID_ARGUMENT
+    # top-k: row stride shorter than the row
+    v = ctypes.c_void_p(16)
+    assert L.dsa_topk(ctypes.byref(p), v, 100, v, None) == dsa.DSA_ERR_INVALID_ARGUMENT
+    # attention: too small a workspace for the decode split
+    need = dsa.workspace_size(p, dsa.DSA_OP_ATTN)
+    assert need > 0
+    assert L.dsa_sparse_mla_attn(ctypes.byref(p), v, v, v, v, None, v, need - 1, None) == \
+        dsa.DSA_ERR_WORKSPACE_TOO_SMALL
+    # timed forward: events requested but missing
+    assert L.dsa_forward_timed(ctypes.byref(p), v, None, v, None, v, v, v, None, v, None, v, 1 << 40,
+                               None, 8, None, None) == dsa.DSA_ERR_INVALID_ARGUMENT
