@@ -123,9 +123,10 @@ dsa_status_t dsa_topk(const dsa_problem_t* prob, const float* scores, int64_t ro
  *   q_attn   [B][Lq][NH][Dqk] attn_dtype
  *   kv       [B][Lk][Dqk]     attn_dtype; one latent row per token, shared
  *                             by all NH heads; values = its leading Dv dims
- *   topk_idx [B][Lq][K]       int32 positions; entries < 0 are skipped; every
- *                             entry >= 0 must be < Lk (not checked on device);
- *                             each row must hold at least one entry >= 0
+ *   topk_idx [B][Lq][K]       int32 positions; entries < 0 or >= Lk are
+ *                             skipped, repeated entries count repeatedly; a
+ *                             row with no usable entry gives out = 0 and
+ *                             lse = -inf
  *   out      [B][Lq][NH][Dv]  out_dtype:
  *       out[a] = sum_j softmax_j(scale * q_a . kv_j) * kv_j[0:Dv] over chosen j
  *   lse      [B][Lq][NH] fp32 natural-log sum-exp of the scaled logits, or NULL
@@ -153,11 +154,11 @@ dsa_status_t dsa_forward(const dsa_problem_t* prob,
                          hipStream_t stream);
 
 /* dsa_forward with per-kernel timing events (for measurement).
- *   events: caller-created hipEvent_t handles, 2 per launch slot:
- *     events[2*(c*DSA_NUM_STAGES + s)] recorded before, and
+ *   events: n_events caller-created hipEvent_t handles, 2 per launch slot:
+ *     events[2*(c*DSA_NUM_STAGES + s)] is recorded on `stream` before, and
  *     events[2*(c*DSA_NUM_STAGES + s) + 1] after, the launch of stage s for
- *     query chunk c, for c < n_event_slots / (2*DSA_NUM_STAGES).  Stages
- *     that do not run in a chunk record both events back to back.
+ *     query chunk c, for every slot that fits in n_events.  Stages that do
+ *     not run in a chunk record both events back to back.
  *   n_chunks_out: if not NULL, receives the number of query chunks used.
  */
 #define DSA_NUM_STAGES 4   /* 0 indexer, 1 top-k, 2 attention, 3 split combine */
@@ -168,7 +169,7 @@ dsa_status_t dsa_forward_timed(const dsa_problem_t* prob,
                                const void* q_attn, const void* kv,
                                int32_t* topk_idx, void* out, float* lse,
                                void* workspace, size_t workspace_bytes,
-                               hipEvent_t* events, int32_t n_event_slots,
+                               hipEvent_t* events, int32_t n_events,
                                int32_t* n_chunks_out,
                                hipStream_t stream);
 

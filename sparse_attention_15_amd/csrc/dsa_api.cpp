@@ -266,10 +266,10 @@ dsa_status_t dsa_forward(const dsa_problem_t* prob, const void* q_idx, const uin
 dsa_status_t dsa_forward_timed(const dsa_problem_t* prob, const void* q_idx, const uint8_t* q_scale,
                                const void* k_idx, const uint8_t* k_scale, const float* head_w, const void* q_attn,
                                const void* kv, int32_t* topk_idx, void* out, float* lse, void* workspace,
-                               size_t workspace_bytes, hipEvent_t* events, int32_t n_event_slots,
+                               size_t workspace_bytes, hipEvent_t* events, int32_t n_events,
                                int32_t* n_chunks_out, hipStream_t stream) {
-  if (n_event_slots < 0 || (n_event_slots > 0 && !events)) return DSA_ERR_INVALID_ARGUMENT;
-  EventSink sink{events, n_event_slots / 2, stream};
+  if (n_events < 0 || (n_events > 0 && !events)) return DSA_ERR_INVALID_ARGUMENT;
+  EventSink sink{events, n_events / 2, stream};
   return forward_impl(prob, q_idx, q_scale, k_idx, k_scale, head_w, q_attn, kv, topk_idx, out, lse, workspace,
                       workspace_bytes, sink, n_chunks_out, stream);
 }

@@ -223,7 +223,7 @@ def sparse_mla_attn(p: Problem, q_attn, kv, topk_idx, out=None, lse=None, worksp
 
 
 def forward(p: Problem, q_idx, q_scale, k_idx, k_scale, head_w, q_attn, kv, out=None, lse=None,
-            topk_idx=None, workspace=None, events=None, n_event_slots: int = 0):
+            topk_idx=None, workspace=None, events=None, n_events: int = 0):
     """Fused scores -> top-k -> sparse attention.  Returns (out, lse, topk_idx).
 
     events: optional ctypes array of hipEvent_t (2 per stage slot) for
@@ -240,7 +240,7 @@ def forward(p: Problem, q_idx, q_scale, k_idx, k_scale, head_w, q_attn, kv, out=
         st = lib().dsa_forward(ctypes.byref(p), *iargs, qa, kvp, ip, op, lp, wsp, ws.numel(), _stream())
     else:
         st = lib().dsa_forward_timed(ctypes.byref(p), *iargs, qa, kvp, ip, op, lp, wsp, ws.numel(),
-                                     events, n_event_slots, None, _stream())
+                                     events, n_events, None, _stream())
     _check(st, "dsa_forward")
     return out, lse, topk_idx
 
