@@ -11,19 +11,21 @@
 // "DeepSeek-V3.2-Exp" token-ids page (n_heads 128, kv_lora_rank 512,
 // qk_rope_head_dim 64).
 //
-// bf16 kernel, one work-group per (query, key split), 8 waves x 16 heads:
+// bf16 kernel, one work-group per (query, key split), 8 waves in 4 pairs:
 //  - the selected rows are gathered from HBM in blocks of 32 straight into
 //    LDS (global_load_lds: each lane moves one 16-byte chunk of a 1152-byte
 //    row, no registers involved), three blocks in flight, and staged once
 //    for all 128 heads;
-//  - S^T = KV_blk . Q^T on 16x16x32 MFMA (Q stays in registers), so each
-//    lane column owns one head and the softmax max/sum are lane-local plus
-//    two cross-lane exchanges;
+//  - S^T = KV_blk . Q^T on 32x32x16 MFMA, the 576 dims split between the two
+//    waves of a pair and the partial tiles summed through LDS (Q stays in
+//    registers); each lane owns one head, so the softmax max/sum are
+//    lane-local plus one cross-half exchange;
 //  - online softmax in base 2, with the running max only raised when a block
 //    exceeds it by more than 2^8 (the accumulator rescale is then rare);
 //  - O^T += V^T . P^T on MFMA with P taken straight from the S^T registers
 //    and the value operand read transposed from the row-major tile
-//    (ds_read_b64_tr_b16), so no second copy of the values is staged.
+//    (ds_read_b64_tr_b16), so no second copy of the values is staged; the
+//    two partners cover the two halves of the 512 value dims.
 // Decode-shaped launches split each query's list over several work-groups
 // and merge the partial (O, lse) pairs in a second kernel.
 #include "dsa_device.h"
@@ -40,22 +42,24 @@ constexpr float kLn2 = 0.6931471805599453f;
 constexpr int kNH = 128, kDqk = 576, kDv = 512, kBK = 32;
 constexpr int kRowB = kDqk * 2;                 // 1152 bytes per kv row = 72 chunks of 16 B
 constexpr int kChunks = kRowB / 16;
-constexpr int kStageBytes = kBK * kRowB;        // one 32-row block in LDS
-constexpr int kMaxPer = 4096;                   // list entries per work-group
+constexpr int kLdsChunks = 76;                  // LDS row stride in 16-byte chunks (4 unused)
+constexpr int kLdsRow = kLdsChunks * 16;
+constexpr int kStageBytes = kBK * kLdsRow;      // one 32-row block in LDS
+constexpr int kDmaInstr = kBK * kLdsChunks / 64;  // 38 gather instructions per block
+constexpr int kMaxPer = 2048;                   // list entries per work-group
 constexpr float kTau = 8.0f;                    // lazy max threshold (log2 units)
 
 #define LDS_PTR(p) ((__attribute__((address_space(3))) void*)(p))
 #define GLB_PTR(p) ((const __attribute__((address_space(1))) void*)(p))
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 
-// Rows of a staged block sit back to back (1152 B = 8 bank quads mod 16);
-// the 16-byte chunk c of row r is stored at chunk c ^ swz(r), which keeps
-// both the 16-row MFMA operand reads (one chunk of 16 consecutive rows) and
-// the transposed value reads (two chunks of 4 rows) on distinct bank quads.
-__device__ __forceinline__ int swz(int r) {
-  const int j = (r >> 1) & 7;
-  return (j >> 1) | ((j & 1) << 2);
-}
+// A staged block holds 32 rows of 76 16-byte chunks (72 used).  The row
+// stride and the chunk permutation (chunk c of row r stored at c ^ swz(r),
+// swz(r) < 4, i.e. within aligned groups of four) were chosen by measuring
+// both operand read patterns on gfx950: they spread the rows of a 32-row QK
+// operand read and the 8-row transposed value reads over the LDS banks, and
+// keep every operand address a per-lane base plus a compile-time offset.
+__device__ __forceinline__ int swz(int r) { return ((r >> 2) + 1) & 3; }
 
 // s_waitcnt on the vector-memory counter only (gfx9 encoding: expcnt and
 // lgkmcnt fields left at their maxima).
@@ -83,91 +87,132 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) uint8_t*)(p);
 }
 
+// max over lanes l and l ^ 32 (v_permlane32_swap exchanges the two halves
+// of the wave without going through LDS)
+__device__ __forceinline__ float max_xor32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, x), __builtin_bit_cast(uint32_t, x),
+                                                  false, false);
+  return fmaxf(__builtin_bit_cast(float, r[0]), __builtin_bit_cast(float, r[1]));
+}
+
 __device__ __forceinline__ u32x2 tr_read(const uint8_t* p) {
   const i16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(p));
   return __builtin_bit_cast(u32x2, v);
 }
 
-// Work split: 8 waves x 16 heads.  Per wave and 32-key block, on 16x16x32
-// MFMA: S^T (2 key tiles x 16 heads, 18 k-steps over 576 dims) and
-// O^T (32 value tiles x 16 heads, one k-step over the 32 keys).
-// Lane l: column = head 16*wave + (l % 16), k-group g = l / 16.
-//   S^T rows (keys) held: 4g + i and 16 + 4g + i, i = 0..3.
-//   O^T rows (value dims) held: 16*vt + 4g + i.
+// Work split: 8 waves = 4 pairs; pair p owns heads 32p .. 32p+31 and the two
+// partners split the work, per 32-key block, on 32x32x16 MFMA:
+//   QK: partner d computes the partial S^T over dims [288d, 288d + 288)
+//       (18 k-steps; its Q^T fragments stay in 72 registers), writes it to
+//       LDS, and after a barrier adds the other partner's partial, so both
+//       hold the same full S^T (fp32 addition commutes);
+//   softmax: done identically by both partners;
+//   PV: partner d accumulates O^T for value dims [256d, 256d + 256).
+// Lane l: column = head 32p + (l % 32), half hf = l / 32.
+//   S^T rows (keys) held: 8q + 4hf + r, q, r = 0..3.
+//   O^T rows (value dims) held: 256d + 32vt + 8q + 4hf + r.
 constexpr int kWavesA = 8;
-constexpr int kQRegSteps = 16;                  // k-steps of Q kept in registers (latent dims)
+constexpr int kQSteps = 18;                      // 16-dim k-steps per partner
+constexpr int kVTiles = 8;                       // 32-wide value tiles per partner
 struct AttnState {
-  u32x4 qf[kQRegSteps];  // Q^T fragments (B operand): dims 32t + 8g .. +8 of this lane's head
-  f32x4 o[32];         // O^T accumulators
+  u32x4 qf[kQSteps];   // Q^T fragments (B operand)
+  f32x16 o[kVTiles];   // O^T accumulators
   float m_run, l_run;
 };
 
-// Gather instructions per wave per block: 36 x 64-lane 16-byte copies
-// split 5,5,5,5,4,4,4,4 over the 8 waves.
-__device__ __forceinline__ int dma_first(int wave) { return wave < 4 ? 5 * wave : 20 + 4 * (wave - 4); }
+// Gather instructions per wave per block: 38 x 64-lane 16-byte copies
+// split 5,5,5,5,5,5,4,4 over the 8 waves.
+__device__ __forceinline__ int dma_first(int wave) { return wave < 6 ? 5 * wave : 30 + 4 * (wave - 6); }
+static_assert(kDmaInstr == 38, "gather split assumes 38 instructions per block");
 
-// One 32-row block: S^T = KV.Q^T, online softmax, O^T += V^T.P^T.
-__device__ __forceinline__ void attn_block(AttnState& st, const uint8_t* buf, const int* bpos,
-                                           const uint8_t* qrope, const int (&qk_off)[2][2],
-                                           const int (&pv_off)[2][4], int g, float zscale) {
-  f32x4 s[2];
+// One 32-row block.
+__device__ __forceinline__ void attn_block(AttnState& st, const uint8_t* buf, uint32_t vmask, float* exch_mine,
+                                           const float* exch_other, const int (&qk_off)[2],
+                                           const int (&pv_off)[2][2], int hf, float zscale) {
+  f32x16 s;
 #pragma unroll
-  for (int m = 0; m < 2; ++m) s[m] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int e = 0; e < 16; ++e) s[e] = 0.f;
 #pragma unroll
-  for (int t = 0; t < 18; ++t) {
-    const u32x4 qb = t < kQRegSteps ? st.qf[t < kQRegSteps ? t : 0] : ld16(qrope + 64 * (t - kQRegSteps));
+  for (int t = 0; t < kQSteps; ++t) s = mfma32(ld16(buf + qk_off[t & 1] + 64 * (t >> 1)), st.qf[t], s);
+  // exchange partial scores with the partner wave (lane-linear, 4 x 16 B)
 #pragma unroll
-    for (int m = 0; m < 2; ++m)
-      s[m] = mfma16(ld16(buf + qk_off[m][t & 1] + 128 * (t >> 1)), qb, s[m]);
+  for (int q = 0; q < 4; ++q) {
+    const f32x4 v = {s[4 * q], s[4 * q + 1], s[4 * q + 2], s[4 * q + 3]};
+    *reinterpret_cast<f32x4*>(exch_mine + q * 256) = v;
   }
-  float z[8];
+  __builtin_amdgcn_s_waitcnt(0xc07f);             // lgkmcnt(0)
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
 #pragma unroll
-  for (int m = 0; m < 2; ++m) {
-    const u32x4 pv = *reinterpret_cast<const u32x4*>(bpos + 16 * m + 4 * g);
-#pragma unroll
-    for (int r = 0; r < 4; ++r) z[4 * m + r] = ((int)pv[r] >= 0) ? s[m][r] * zscale : kNegInf;
+  for (int q = 0; q < 4; ++q) {
+    const f32x4 v = *reinterpret_cast<const f32x4*>(exch_other + q * 256);
+    s[4 * q] += v[0];
+    s[4 * q + 1] += v[1];
+    s[4 * q + 2] += v[2];
+    s[4 * q + 3] += v[3];
   }
-  float mb = z[0];
+  // scaled base-2 logits; keys not listed in this block (bit clear in
+  // vmask) get -inf.  This lane's keys: 8q + 4hf + r.
 #pragma unroll
-  for (int e = 1; e < 8; ++e) mb = fmaxf(mb, z[e]);
-  mb = fmaxf(mb, shfl_xor(mb, 16));
-  mb = fmaxf(mb, shfl_xor(mb, 32));
+  for (int e = 0; e < 16; ++e) s[e] *= zscale;
+  if (vmask != 0xffffffffu) {
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const int key = 8 * (e >> 2) + 4 * hf + (e & 3);
+      s[e] = ((vmask >> key) & 1u) ? s[e] : kNegInf;
+    }
+  }
+  float mb = fmaxf(fmaxf(s[0], s[1]), s[2]);
+#pragma unroll
+  for (int e = 3; e < 15; e += 2) mb = fmaxf(fmaxf(mb, s[e]), s[e + 1]);
+  mb = fmaxf(mb, s[15]);
+  mb = max_xor32(mb);
   if (__ballot(mb > st.m_run + kTau)) {
     const float m_new = fmaxf(st.m_run, mb);
-    const float alpha = (st.m_run == kNegInf) ? 0.f : exp2f(st.m_run - m_new);
+    const float alpha = (st.m_run == kNegInf) ? 0.f : __builtin_amdgcn_exp2f(st.m_run - m_new);
 #pragma unroll
-    for (int v = 0; v < 32; ++v) st.o[v] *= alpha;
+    for (int v = 0; v < kVTiles; ++v) st.o[v] *= alpha;
     st.l_run *= alpha;
     st.m_run = m_new;
   }
   const float mref = (st.m_run == kNegInf) ? 0.f : st.m_run;
-  u32x4 pb;
+  // p = 2^(z - m) <= 2^kTau; P is rounded to bf16 for the MFMA, the
+  // normaliser sums the fp32 values (the rounding is unbiased and far below
+  // the output rounding)
+  u32x4 pb[2];
   float lsum = 0.f;
 #pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    const uint32_t u = pack_bf16x2(exp2f(z[2 * e] - mref), exp2f(z[2 * e + 1] - mref));
-    pb[e] = u;
-    lsum += bf16_lo(u) + bf16_hi(u);
-  }
-  st.l_run += lsum;
+  for (int k = 0; k < 2; ++k)
 #pragma unroll
-  for (int vt = 0; vt < 32; ++vt) {
-    const int imm = 128 * (vt >> 2);
-    const u32x2 lo = tr_read(buf + pv_off[0][vt & 3] + imm);
-    const u32x2 hi = tr_read(buf + pv_off[1][vt & 3] + imm);
-    const u32x4 av = {lo[0], lo[1], hi[0], hi[1]};
-    st.o[vt] = mfma16(av, pb, st.o[vt]);
-  }
+    for (int e = 0; e < 4; ++e) {
+      const float p0 = __builtin_amdgcn_exp2f(s[8 * k + 2 * e] - mref);
+      const float p1 = __builtin_amdgcn_exp2f(s[8 * k + 2 * e + 1] - mref);
+      pb[k][e] = pack_bf16x2(p0, p1);
+      lsum += p0 + p1;
+    }
+  st.l_run += lsum;
+  // O^T[v][head] += V^T[v][key] . P^T[key][head]
+#pragma unroll
+  for (int vt = 0; vt < kVTiles; ++vt)
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      const u32x2 lo = tr_read(buf + pv_off[k][0] + 64 * vt);
+      const u32x2 hi = tr_read(buf + pv_off[k][1] + 64 * vt);
+      const u32x4 av = {lo[0], lo[1], hi[0], hi[1]};
+      st.o[vt] = mfma32(av, pb[k], st.o[vt]);
+    }
 }
 
 __global__ __launch_bounds__(kWavesA * 64, 1) void attn_bf16_kernel(AttnLaunch a) {
   __shared__ __attribute__((aligned(16))) uint8_t stg[3 * kStageBytes];
   __shared__ __attribute__((aligned(16))) int spos[kMaxPer];
-  __shared__ __attribute__((aligned(16))) uint8_t qrope_s[kNH * 128];   // rope dims of Q, per head
+  __shared__ uint32_t bmask[kMaxPer / kBK];       // per 32-entry block: bit j = entry j usable
+  __shared__ __attribute__((aligned(16))) float exch[kWavesA * 1024];   // 4 KiB of partial scores per wave
   __shared__ int s_last;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int g = lane >> 4, c16 = lane & 15;
+  const int hf = lane >> 5, c32 = lane & 31;
+  const int pair = wave >> 1, d = wave & 1;
   const int split = blockIdx.x;
   const int rr = gridDim.y - 1 - blockIdx.y;    // launch row; latest queries first
   const int b = rr / a.q_count;
@@ -191,78 +236,101 @@ __global__ __launch_bounds__(kWavesA * 64, 1) void attn_bf16_kernel(AttnLaunch a
   if (my_last >= 0) atomicMax(&s_last, my_last);
 
   AttnState st;
-  const int h = 16 * wave + c16;
+  const int h = 32 * pair + c32;
   {
-    const uint8_t* qb = static_cast<const uint8_t*>(a.qa) + (qrow * kNH + h) * (int64_t)kRowB;
+    const uint8_t* qb = static_cast<const uint8_t*>(a.qa) + (qrow * kNH + h) * (int64_t)kRowB + 576 * d;
 #pragma unroll
-    for (int t = 0; t < kQRegSteps; ++t) st.qf[t] = ld16(qb + (32 * t + 8 * g) * 2);
-    // rope k-steps: head h's 64 dims (8 chunks) at qrope_s + 128h; this
-    // lane's chunk for k-step 16 + u is 4u + g
-#pragma unroll
-    for (int u = 0; u < 18 - kQRegSteps; ++u)
-      st16(qrope_s + 128 * h + 16 * (4 * u + g), ld16(qb + (32 * (kQRegSteps + u) + 8 * g) * 2));
+    for (int t = 0; t < kQSteps; ++t) st.qf[t] = ld16(qb + (16 * t + 8 * hf) * 2);
   }
 #pragma unroll
-  for (int v = 0; v < 32; ++v) st.o[v] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int v = 0; v < kVTiles; ++v)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) st.o[v][e] = 0.f;
   st.m_run = kNegInf;
   st.l_run = 0.f;
   const float zscale = a.scale * kLog2e;
 
-  // QK operand: key row 16m + c16, logical chunk 4t + g, stored at
-  // (4t + g) ^ swz(row) = 4 * (t ^ (y >> 2)) + (y & 3) with y = g ^ swz(row).
-  int qk_off[2][2];
-#pragma unroll
-  for (int m = 0; m < 2; ++m) {
-    const int row = 16 * m + c16;
-    const int y = g ^ swz(row);
-    const int base = row * kRowB + 16 * (y & 3);
-    const int flip = (y >> 2) ? 64 : 0;
-    qk_off[m][0] = base + flip;                    // even t: 64t = 128(t>>1)
-    qk_off[m][1] = base + 64 - flip;               // odd t:  64t = 128(t>>1) + 64
-  }
-  // PV operand (transposed reads): group g = lane/16 takes keys 4g + e
-  // (first read) and 16 + 4g + e (second); source lane j = lane%16 reads
-  // row key0 + j/4, value columns 16vt + 4(j&3) .. +3, i.e. logical chunk
-  // 2vt + ((j&3) >> 1), half (j & 1).  Stored chunk (2vt + x) ^ swz(row)
-  // = 2 * (vt ^ (y >> 1)) + (y & 1), y = x ^ swz(row).
-  int pv_off[2][4];
+  // QK operand: key row c32, logical chunk 36d + 2t + hf
+  //   = 36d + 4(t >> 1) + (2(t & 1) + hf), stored with the low two bits
+  //   XOR swz(row): offset qk_off[t & 1] + 64 * (t >> 1).
+  int qk_off[2];
   {
-    const int x = (c16 & 3) >> 1, within = (c16 & 1) * 8;
+    const int f = swz(c32);
 #pragma unroll
-    for (int w = 0; w < 2; ++w) {
-      const int row = 16 * w + 4 * g + (c16 >> 2);
-      const int y = x ^ swz(row);
+    for (int par = 0; par < 2; ++par) qk_off[par] = c32 * kLdsRow + 576 * d + 16 * ((2 * par + hf) ^ f);
+  }
+  // PV operand (transposed reads) for 32x32x16: 16-lane group G holds value
+  // rows 16(G&1) + j of the tile and k-half G>>1.  Step k, part w (lo/hi)
+  // reads key row 16k + 8w + 4(G>>1) + j/4, value columns
+  // 256d + 32vt + 16(G&1) + 4(j&3) .. +3: logical chunk 32d + 4vt + k0 with
+  // k0 = 2(G&1) + (j&3)/2, byte (j&1)*8; stored at 32d + 4vt + (k0 ^ swz):
+  // offset pv_off[k][w] + 64 * vt.
+  int pv_off[2][2];
+  {
+    const int G = lane >> 4, j = lane & 15;
+    const int k0 = 2 * (G & 1) + ((j & 3) >> 1), within = (j & 1) * 8;
 #pragma unroll
-      for (int k = 0; k < 4; ++k) pv_off[w][k] = row * kRowB + 16 * (y & 1) + within + 32 * (k ^ (y >> 1));
-    }
+    for (int k = 0; k < 2; ++k)
+#pragma unroll
+      for (int w = 0; w < 2; ++w) {
+        const int row = 16 * k + 8 * w + 4 * (G >> 1) + (j >> 2);
+        pv_off[k][w] = row * kLdsRow + 16 * (32 * d + (k0 ^ swz(row))) + within;
+      }
   }
   __syncthreads();
   const int nblk = (s_last + kBK) / kBK;          // blocks up to the last listed entry
+  // Consume the Q fragments here so that their loads are complete before the
+  // loop: the compiler's own vector-memory waits would otherwise stay inside
+  // the loop and also stall on the in-flight row gathers.
+#pragma unroll
+  for (int t = 0; t < kQSteps; ++t) asm volatile("" : "+v"(st.qf[t]));
+  for (int blk = wave; blk < nblk; blk += kWavesA) {
+    const uint64_t bal = __ballot(lane < kBK && spos[blk * kBK + (lane & (kBK - 1))] >= 0);
+    if (lane == 0) bmask[blk] = (uint32_t)bal;
+  }
+  __syncthreads();
 
   // Gather map: instruction k of this wave fills LDS chunk slots
-  // f = (dma_first(wave) + k)*64 + lane: row f/72, stored chunk f%72, which
-  // holds logical chunk (f%72) ^ swz(row).
+  // f = (dma_first(wave) + k)*64 + lane: row f/76, stored chunk f%76 (slots
+  // 72..75 are padding and stay unloaded), which holds logical chunk
+  // (f%76) ^ swz(row).
   const int dfirst = dma_first(wave);
-  const int dcount = wave < 4 ? 5 : 4;
+  const int dcount = wave < 6 ? 5 : 4;
+  // per lane and gather instruction: row (low 8 bits) | stored-chunk byte
+  // offset << 8, or ~0u for a padding slot
+  uint32_t dma_map[5];
+#pragma unroll
+  for (int k = 0; k < 5; ++k) {
+    const int f = (dfirst + k) * 64 + lane;
+    const int r = f / kLdsChunks, p = f - r * kLdsChunks;
+    dma_map[k] = p < kChunks ? ((uint32_t)r | ((uint32_t)((p ^ swz(r)) << 4) << 8)) : ~0u;
+  }
   const uint8_t* kvb = static_cast<const uint8_t*>(a.kv) + (int64_t)b * a.Lk * kRowB;   // uniform
   const uint32_t stg_lds = lds_addr(stg);
   auto issue = [&](int blk, int sb) {
     const uint32_t dst = __builtin_amdgcn_readfirstlane(stg_lds + sb * kStageBytes);
+    const int* bp = spos + blk * kBK;
+    uint32_t voff[5];
+#pragma unroll
+    for (int k = 0; k < 5; ++k) {               // all position reads first: one LDS latency
+      uint32_t m = dma_map[k];
+      asm volatile("" : "+v"(m));               // keep the packed form (one register)
+      voff[k] = m == ~0u ? ~0u : (uint32_t)max(bp[m & 0xffu], 0) * kRowB + (m >> 8);
+    }
 #pragma unroll
     for (int k = 0; k < 5; ++k) {
       if (k < dcount) {
-        const int f = (dfirst + k) * 64 + lane;
-        const int r = f / kChunks, p = f - r * kChunks;
-        const int pos = max(spos[blk * kBK + r], 0);
-        dma16(kvb, (uint32_t)pos * kRowB + ((p ^ swz(r)) << 4),
-              __builtin_amdgcn_readfirstlane(dst + (dfirst + k) * 1024));
+        const uint32_t ldst = __builtin_amdgcn_readfirstlane(dst + (dfirst + k) * 1024);
+        if (voff[k] != ~0u) dma16(kvb, voff[k], ldst);
       }
     }
   };
+  float* exch_mine = exch + wave * 1024 + lane * 4;
+  const float* exch_other = exch + (wave ^ 1) * 1024 + lane * 4;
   // Block blk lives in stage buffer blk % 3.  Wait for its gather (the next
   // block's may stay in flight), barrier (every wave is then also done with
-  // block blk-1's buffer), start the gather two blocks ahead into that
-  // buffer, then compute.
+  // block blk-1's buffer and scores exchange), start the gather two blocks
+  // ahead into that buffer, then compute.
   if (nblk > 0) issue(0, 0);
   if (nblk > 1) issue(1, 1);
   int sb = 0;
@@ -277,35 +345,50 @@ __global__ __launch_bounds__(kWavesA * 64, 1) void attn_bf16_kernel(AttnLaunch a
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
     if (blk + 2 < nblk) issue(blk + 2, sb == 0 ? 2 : sb - 1);
-    attn_block(st, stg + sb * kStageBytes, spos + blk * kBK, qrope_s + 128 * h + 16 * g, qk_off, pv_off, g,
-               zscale);
+    const uint32_t vmask = __builtin_amdgcn_readfirstlane(bmask[blk]);
+    attn_block(st, stg + sb * kStageBytes, vmask, exch_mine, exch_other, qk_off, pv_off, hf, zscale);
     sb = sb == 2 ? 0 : sb + 1;
   }
 
-  float l_tot = st.l_run + shfl_xor(st.l_run, 16);
-  l_tot += shfl_xor(l_tot, 32);
+  const float l_tot = st.l_run + shfl_xor(st.l_run, 32);
   const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
   const float lse = l_tot > 0.f ? (st.m_run + log2f(l_tot)) * kLn2 : kNegInf;
+  const int vbase = 256 * d + 4 * hf;
   if (a.splits == 1) {
     if (a.out_f32) {
-      float* op = static_cast<float*>(a.out) + (qrow * kNH + h) * kDv + 4 * g;
+      float* op = static_cast<float*>(a.out) + (qrow * kNH + h) * kDv + vbase;
 #pragma unroll
-      for (int vt = 0; vt < 32; ++vt) *reinterpret_cast<f32x4*>(op + 16 * vt) = st.o[vt] * inv;
+      for (int vt = 0; vt < kVTiles; ++vt)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const f32x4 v4 = {st.o[vt][4 * q] * inv, st.o[vt][4 * q + 1] * inv, st.o[vt][4 * q + 2] * inv,
+                            st.o[vt][4 * q + 3] * inv};
+          *reinterpret_cast<f32x4*>(op + 32 * vt + 8 * q) = v4;
+        }
     } else {
-      uint16_t* op = static_cast<uint16_t*>(a.out) + (qrow * kNH + h) * kDv + 4 * g;
+      uint16_t* op = static_cast<uint16_t*>(a.out) + (qrow * kNH + h) * kDv + vbase;
 #pragma unroll
-      for (int vt = 0; vt < 32; ++vt) {
-        const f32x4 v = st.o[vt] * inv;
-        *reinterpret_cast<u32x2*>(op + 16 * vt) = u32x2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
-      }
+      for (int vt = 0; vt < kVTiles; ++vt)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const u32x2 v2 = {pack_bf16x2(st.o[vt][4 * q] * inv, st.o[vt][4 * q + 1] * inv),
+                            pack_bf16x2(st.o[vt][4 * q + 2] * inv, st.o[vt][4 * q + 3] * inv)};
+          *reinterpret_cast<u32x2*>(op + 32 * vt + 8 * q) = v2;
+        }
     }
-    if (a.lse && g == 0) a.lse[qrow * kNH + h] = lse;
+    if (a.lse && hf == 0 && d == 0) a.lse[qrow * kNH + h] = lse;
   } else {
     const int64_t prow = (int64_t)rr * a.splits + split;
-    float* op = a.part_o + (prow * kNH + h) * kDv + 4 * g;
+    float* op = a.part_o + (prow * kNH + h) * kDv + vbase;
 #pragma unroll
-    for (int vt = 0; vt < 32; ++vt) *reinterpret_cast<f32x4*>(op + 16 * vt) = st.o[vt] * inv;
-    if (g == 0) a.part_lse[prow * kNH + h] = lse;
+    for (int vt = 0; vt < kVTiles; ++vt)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const f32x4 v4 = {st.o[vt][4 * q] * inv, st.o[vt][4 * q + 1] * inv, st.o[vt][4 * q + 2] * inv,
+                          st.o[vt][4 * q + 3] * inv};
+        *reinterpret_cast<f32x4*>(op + 32 * vt + 8 * q) = v4;
+      }
+    if (hf == 0 && d == 0) a.part_lse[prow * kNH + h] = lse;
   }
 }
 
