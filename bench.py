@@ -1,10 +1,13 @@
 """Throughput of the fused DSA hot path (indexer -> top-k -> sparse MLA) on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--config NAME] [--no-cpu-baseline]
+    python bench.py --copy-calibration      (a 1 GiB copy, for scaling byte counters)
 
 A step is one dsa_forward call over one batch of synthetic inputs already
 resident in HBM.  Input sets rotate between steps so that repeated steps do
-not hit data left in the 256 MB Infinity Cache.  Prints one JSON line.
+not hit data left in the 256 MB Infinity Cache.  The timed region is `steps`
+plain calls; per-kernel durations come from the same number of calls again
+with a HIP event pair around every launch.  Prints one JSON line.
 """
 from __future__ import annotations
 
@@ -41,22 +44,73 @@ def algorithmic(cfg):
                 index_flops=2 * H * D * pairs, attn_flops=2 * NH * (Dqk + Dv) * sel)
 
 
+# kernel -> (source file, stage index)
+KERNELS = {
+    "idx_decode_kernel": ("indexer.hip", 0),
+    "idx_prefill_kernel": ("indexer.hip", 0),
+    "idx_f32_kernel": ("indexer.hip", 0),
+    "topk_kernel": ("topk.hip", 1),
+    "attn_bf16_kernel": ("sparse_mla.hip", 2),
+    "attn_f32_kernel": ("sparse_mla.hip", 2),
+    "attn_combine_kernel": ("sparse_mla.hip", 3),
+}
+
+
 def source_hash(name):
     with open(os.path.join(ROOT, "sparse_attention_15_amd", "csrc", name), "rb") as f:
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
-def measured_traffic(kernel_src, workload):
-    """HBM bytes per launch from committed rocprofv3 counter summaries, if the
-    kernel source is unchanged since they were taken; else None."""
-    path = os.path.join(ROOT, "profiles", "traffic.json")
+def measured_traffic(kernel, workload):
+    """HBM bytes per launch of `kernel` on `workload` from the committed
+    rocprofv3 counter summary (FETCH_SIZE + WRITE_SIZE, copy-calibrated), if
+    the kernel's source is unchanged since the counters were taken; else None."""
+    path = os.path.join(ROOT, "profiles", f"{kernel}.{workload}.traffic.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
-        rec = json.load(f).get(workload)
-    if not rec or rec.get("source_sha256_16") != source_hash(kernel_src):
+        rec = json.load(f)
+    if rec.get("source_sha256_16") != source_hash(KERNELS[kernel][0]):
         return None
     return rec.get("bytes_per_launch")
+
+
+def stage_kernels(cfg):
+    """Kernel that runs in each stage of dsa_forward for this workload."""
+    decode = cfg.q_len <= 4
+    if cfg.index_dtype == "f32":
+        return ["idx_f32_kernel", "topk_kernel", "attn_f32_kernel", "attn_combine_kernel"]
+    return ["idx_decode_kernel" if decode else "idx_prefill_kernel", "topk_kernel", "attn_bf16_kernel",
+            "attn_combine_kernel"]
+
+
+def kernel_units(cfg, kernel, al, n_chunks, split_rows):
+    """(bound, algorithmic units per launch, unit, peak, description) of one kernel."""
+    B, Lq, Lk, K = cfg.batch, cfg.q_len, cfg.kv_len, cfg.topk
+    NH, Dv = cfg.attn_heads, cfg.v_dim
+    decode = Lq <= 4
+    if kernel.startswith("idx_"):
+        if decode or cfg.index_dtype == "f32":
+            return ("hbm", al["index_bytes"] / n_chunks, "GB/s", HBM_PEAK_GBS,
+                    "algorithmic bytes per launch: index keys + index q + head weights (+ scales)")
+        peak = MFMA_FP8_PEAK_TFLOPS if cfg.index_dtype == "fp8_e4m3" else MFMA_BF16_PEAK_TFLOPS
+        return ("mfma", al["index_flops"] / n_chunks, "TFLOP/s", peak,
+                "algorithmic flops per launch: 2*H*D per visible (query, key) pair")
+    if kernel == "topk_kernel":
+        return ("hbm", 4 * al["pairs"] / n_chunks, "GB/s", HBM_PEAK_GBS,
+                "algorithmic bytes per launch: one fp32 score per visible (query, key) pair")
+    if kernel.startswith("attn_") and kernel != "attn_combine_kernel":
+        if decode:
+            return ("hbm", al["attn_bytes"] / n_chunks, "GB/s", HBM_PEAK_GBS,
+                    "algorithmic bytes per launch: selected latent rows + q + out + lse")
+        return ("mfma", al["attn_flops"] / n_chunks, "TFLOP/s", MFMA_BF16_PEAK_TFLOPS,
+                "algorithmic flops per launch: 2*NH*(Dqk+Dv) per selected (query, key) pair")
+    # combine: read the fp32 partials of every split, write out and lse
+    ob = 4 if cfg.index_dtype == "f32" else 2
+    rows = B * Lq / n_chunks
+    byts = rows * NH * (split_rows * (Dv * 4 + 4) + Dv * ob + 4)
+    return ("hbm", byts, "GB/s", HBM_PEAK_GBS,
+            "bytes per launch: fp32 split partials read + out and lse written")
 
 
 class _Same:
@@ -69,41 +123,68 @@ class _Same:
         return self.a
 
 
-def cpu_baseline(cfg, inp, budget_s=20.0):
-    """The oracle (unchanged) on a bounded sample of the same workload."""
+def cpu_baseline(cfg, sets, budget_s=12.0):
+    """The oracle (unchanged) on a bounded sample of the same workload: query
+    rows in a fixed order, cycling over the input sets, until about budget_s
+    seconds of oracle time (at least one row)."""
     import numpy as np
     import threadpoolctl
+    import torch
     from oracle import dsa_oracle as O
 
     def host(t):
         if t is None:
             return None
-        return t.cpu().numpy() if t.dtype == __import__("torch").uint8 else t.float().cpu().numpy().astype(np.float64)
+        return t.cpu().numpy() if t.dtype == torch.uint8 else t.float().cpu().numpy().astype(np.float64)
 
     rows = [(b, i) for b in range(cfg.batch) for i in range(cfg.q_len)]
     if cfg.q_len > 4:   # prefill: spread the sample over the causal range, latest rows first
         rows = rows[::-1][::max(1, len(rows) // 64)]
     info = threadpoolctl.threadpool_info()
     threads = max(p["num_threads"] for p in info) if info else 1
-    seq = {}
-    done = 0
-    el = 0.0
-    for (b, i) in rows:
-        if b not in seq:          # host copy of this sequence's caches (not timed)
-            seq = {b: {k: host(inp[k][b]) if inp[k] is not None else None for k in ("k_idx", "k_scale", "kv")}}
-        q = {k: host(inp[k][b, i]) if inp[k] is not None else None for k in ("q_idx", "q_scale", "head_w", "q_attn")}
-        wrap = lambda a: None if a is None else _Same(a)  # noqa: E731
-        t0 = time.perf_counter()
-        O.forward_rows(wrap(q["q_idx"]), wrap(q["q_scale"]), wrap(seq[b]["k_idx"]), wrap(seq[b]["k_scale"]),
-                       wrap(q["head_w"]), wrap(q["q_attn"]), wrap(seq[b]["kv"]), [(b, i)],
-                       cfg.q_len, cfg.topk, cfg.softmax_scale, cfg.v_dim)
-        el += time.perf_counter() - t0
-        done += 1
-        if el > budget_s:
-            break
+    cache_key, seq = None, None
+    done, el = 0, 0.0
+    passes = 0
+    while el <= budget_s:
+        for si, inp in enumerate(sets):
+            for (b, i) in rows:
+                if cache_key != (si, b):          # host copy of this sequence's caches (not timed)
+                    seq = {k: host(inp[k][b]) if inp[k] is not None else None for k in ("k_idx", "k_scale", "kv")}
+                    cache_key = (si, b)
+                q = {k: host(inp[k][b, i]) if inp[k] is not None else None
+                     for k in ("q_idx", "q_scale", "head_w", "q_attn")}
+                wrap = lambda a: None if a is None else _Same(a)  # noqa: E731
+                t0 = time.perf_counter()
+                O.forward_rows(wrap(q["q_idx"]), wrap(q["q_scale"]), wrap(seq["k_idx"]), wrap(seq["k_scale"]),
+                               wrap(q["head_w"]), wrap(q["q_attn"]), wrap(seq["kv"]), [(b, i)],
+                               cfg.q_len, cfg.topk, cfg.softmax_scale, cfg.v_dim)
+                el += time.perf_counter() - t0
+                done += 1
+                if el > budget_s:
+                    break
+            if el > budget_s:
+                break
+        passes += 1
     return dict(value=round(done / el, 3), unit="queries/s", cores=int(threads), kind="oracle",
-                sample=f"{done} of {cfg.batch * cfg.q_len} queries of {cfg.name}, fp64 numpy oracle, "
-                       f"{el:.1f} s of oracle time" + ("; rows spread over the causal range" if cfg.q_len > 4 else ""))
+                sample=f"{done} query rows of {cfg.name} ({len(rows)} distinct rows per input set"
+                       + (", spread over the causal range" if cfg.q_len > 4 else "")
+                       + f", {len(sets)} input sets cycled), fp64 numpy oracle, {el:.1f} s of oracle time")
+
+
+def copy_calibration(nbytes=1 << 30, reps=5):
+    """A plain elementwise copy of known size (nbytes read, nbytes written)
+    for scaling the FETCH_SIZE / WRITE_SIZE counters of a rocprofv3 run."""
+    import torch
+    src = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda:0")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        torch.mul(src, 1.0, out=dst)
+    torch.cuda.synchronize()
+    el = (time.perf_counter() - t0) / reps
+    print(json.dumps({"copy_calibration_bytes": nbytes, "reps": reps,
+                      "copy_GBps_read_plus_write": round(2 * nbytes / el / 1e9, 1)}), flush=True)
 
 
 def main():
@@ -115,14 +196,17 @@ def main():
     ap.add_argument("--sets", type=int, default=3, help="rotating input sets")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--out-dtype", default=None)
-    ap.add_argument("--plain-steps", type=int, default=0,
-                    help="also time this many steps without per-kernel events (reported as ms_per_step_plain)")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a 1 GiB elementwise copy (for calibrating rocprofv3 byte counters)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the library has no multi-GPU path, so --gpus must be 1.",
               file=sys.stderr)
         sys.exit(2)
 
+    if args.copy_calibration:
+        copy_calibration()
+        return
     import torch
     import sparse_attention_15_amd as dsa
     from dsa_workloads import BY_NAME, generate
@@ -155,51 +239,46 @@ def main():
         step(k)
     torch.cuda.synchronize()
 
-    # timed region, with per-kernel HIP events recorded on the launch stream
-    events = dsa.StageEvents(args.steps * slots_per_step)
+    # timed region: exactly `steps` calls, no instrumentation
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for k in range(args.steps):
-        step(k, events, base=k * slots_per_step)
+        step(k)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
 
-    plain_ms = None
-    if args.plain_steps > 0:
-        torch.cuda.synchronize()
-        t1 = time.perf_counter()
-        for k in range(args.plain_steps):
-            step(k)
-        torch.cuda.synchronize()
-        plain_ms = (time.perf_counter() - t1) * 1e3 / args.plain_steps
-
+    # per-kernel durations: the same calls again with a HIP event pair around
+    # every launch, recorded on the stream the kernels run on
+    ksteps = args.steps
+    events = dsa.StageEvents(ksteps * slots_per_step)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    for k in range(ksteps):
+        step(k, events, base=k * slots_per_step)
+    torch.cuda.synchronize()
+    evented_ms = (time.perf_counter() - t1) * 1e3 / ksteps
     stage_ms = [0.0] * dsa.DSA_NUM_STAGES
-    for k in range(args.steps):
+    for k in range(ksteps):
         for c in range(n_chunks):
             for st in range(dsa.DSA_NUM_STAGES):
                 stage_ms[st] += events.elapsed_ms(k * slots_per_step + c * dsa.DSA_NUM_STAGES + st)
     events.close()
-    stage_ms = [x / args.steps for x in stage_ms]
-    idx_launch_ms = stage_ms[0] / n_chunks     # average indexer launch duration
+    stage_ms = [x / ksteps for x in stage_ms]
 
     al = algorithmic(cfg)
     ms_per_step = elapsed * 1e3 / args.steps
     qps = cfg.batch * cfg.q_len / (ms_per_step * 1e-3)
-    decode = cfg.q_len <= 4
-    if decode:
-        idx_bytes_launch = al["index_bytes"] / n_chunks
-        achieved = idx_bytes_launch / (idx_launch_ms * 1e-3) / 1e9
-        roof = dict(bound="hbm", achieved=round(achieved, 1), peak=HBM_PEAK_GBS, unit="GB/s",
-                    frac=round(achieved / HBM_PEAK_GBS, 4),
-                    traffic=measured_traffic("indexer.hip", cfg.name), kernel="idx_decode_kernel",
-                    per_launch=f"{idx_bytes_launch} algorithmic bytes (index keys + q + head weights)")
-    else:
-        peak = MFMA_FP8_PEAK_TFLOPS if cfg.index_dtype == "fp8_e4m3" else MFMA_BF16_PEAK_TFLOPS
-        fl_launch = al["index_flops"] / n_chunks
-        achieved = fl_launch / (idx_launch_ms * 1e-3) / 1e12
-        roof = dict(bound="mfma", achieved=round(achieved, 1), peak=peak, unit="TFLOP/s",
-                    frac=round(achieved / peak, 4), traffic=measured_traffic("indexer.hip", cfg.name),
-                    kernel="idx_prefill_kernel", per_launch=f"{fl_launch} algorithmic flops (2*H*D per visible pair)")
+    kernels = stage_kernels(cfg)
+    splits = dsa.attn_splits(p)
+    dom = max(range(dsa.DSA_NUM_STAGES), key=lambda st: stage_ms[st])
+    kname = kernels[dom]
+    launch_ms = stage_ms[dom] / n_chunks               # average launch duration of that kernel
+    bound, units, unit, peak, desc = kernel_units(cfg, kname, al, n_chunks, splits)
+    scale = 1e9 if unit == "GB/s" else 1e12
+    achieved = units / (launch_ms * 1e-3) / scale
+    roof = dict(bound=bound, achieved=round(achieved, 1), peak=peak, unit=unit, frac=round(achieved / peak, 4),
+                traffic=measured_traffic(kname, cfg.name), kernel=kname,
+                launch_us=round(launch_ms * 1e3, 2), per_launch=f"{units:.0f} {desc}")
     path_bytes = al["index_bytes"] + al["attn_bytes"]
     res = {
         "metric": "DSA queries/sec (indexer+top-k+sparse MLA)",
@@ -217,17 +296,17 @@ def main():
         "config": {"workload": cfg.name, "batch": cfg.batch, "q_len": cfg.q_len, "kv_len": cfg.kv_len,
                    "index_heads": cfg.index_heads, "index_dim": cfg.index_dim, "topk": cfg.topk,
                    "attn_heads": cfg.attn_heads, "qk_dim": cfg.qk_dim, "v_dim": cfg.v_dim,
-                   "query_chunks": n_chunks, "input_sets": nsets},
+                   "query_chunks": n_chunks, "attn_splits": splits, "input_sets": nsets},
         "roofline": roof,
         "stage_ms": {name: round(v, 5) for name, v in zip(dsa.STAGE_NAMES, stage_ms)},
-        "ms_per_step_plain": None if plain_ms is None else round(plain_ms, 5),
+        "ms_per_step_evented": round(evented_ms, 5),
         "path_hbm_frac": round(path_bytes / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
         "path_algorithmic_bytes": path_bytes,
         "path_mfma_frac_bf16": round((al["index_flops"] + al["attn_flops"]) / (ms_per_step * 1e-3) / 1e12
                                      / MFMA_BF16_PEAK_TFLOPS, 4),
     }
     if not args.no_cpu_baseline:
-        res["cpu_baseline"] = cpu_baseline(cfg, sets[0])
+        res["cpu_baseline"] = cpu_baseline(cfg, sets)
     print(json.dumps(res), flush=True)
 
 

@@ -183,6 +183,11 @@ size_t dsa_workspace_size(const dsa_problem_t* prob, int32_t op);
 /* Number of query chunks dsa_forward splits this problem into (host only). */
 int32_t dsa_forward_chunks(const dsa_problem_t* prob);
 
+/* Number of work-groups each query's selected list is split over in
+ * dsa_forward's attention step (1: no split, no combine launch); 0 for an
+ * invalid problem.  Host only. */
+int32_t dsa_forward_attn_splits(const dsa_problem_t* prob);
+
 /* Static description of a status code. */
 const char* dsa_status_string(dsa_status_t status);
 

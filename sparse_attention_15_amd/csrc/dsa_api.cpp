@@ -295,6 +295,13 @@ int32_t dsa_forward_chunks(const dsa_problem_t* prob) {
   return plan_forward(*prob, path, true).n_chunks;
 }
 
+int32_t dsa_forward_attn_splits(const dsa_problem_t* prob) {
+  Path path;
+  if (check_problem(prob, &path) != DSA_OK) return 0;
+  const ForwardPlan f = plan_forward(*prob, path, true);
+  return attn_splits(*prob, path, prob->batch * f.chunk);
+}
+
 const char* dsa_status_string(dsa_status_t s) {
   switch (s) {
     case DSA_OK: return "ok";

@@ -71,6 +71,8 @@ def lib() -> ctypes.CDLL:
     L.dsa_workspace_size.restype = SZ
     L.dsa_forward_chunks.argtypes = [P]
     L.dsa_forward_chunks.restype = I32
+    L.dsa_forward_attn_splits.argtypes = [P]
+    L.dsa_forward_attn_splits.restype = I32
     L.dsa_status_string.argtypes = [ctypes.c_int]
     L.dsa_status_string.restype = ctypes.c_char_p
     L.dsa_abi_version.argtypes = []
@@ -184,6 +186,10 @@ def workspace_size(p: Problem, op: int) -> int:
 
 def forward_chunks(p: Problem) -> int:
     return int(lib().dsa_forward_chunks(ctypes.byref(p)))
+
+
+def attn_splits(p: Problem) -> int:
+    return int(lib().dsa_forward_attn_splits(ctypes.byref(p)))
 
 
 def _out_tensor(p: Problem, device):
