@@ -14,6 +14,7 @@ namespace {
 constexpr size_t kAlign = 256;
 constexpr size_t kScoresBudget = size_t(256) << 20;   // bytes of scores per query chunk
 constexpr int64_t kMaxLk = int64_t(1) << 24;
+constexpr int64_t kMaxLkBf16 = int64_t(1) << 21;       // row gathers use 32-bit byte offsets (1152 B rows)
 
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
@@ -42,7 +43,7 @@ dsa_status_t check_problem(const dsa_problem_t* p, Path* path) {
     return DSA_OK;
   }
   if ((it == DSA_BF16 || it == DSA_FP8_E4M3) && at == DSA_BF16 && (ot == DSA_BF16 || ot == DSA_F32)) {
-    if (!is_v32_dims_index(*p) || !is_v32_dims_attn(*p)) return DSA_ERR_UNSUPPORTED;
+    if (!is_v32_dims_index(*p) || !is_v32_dims_attn(*p) || p->kv_len > kMaxLkBf16) return DSA_ERR_UNSUPPORTED;
     *path = it == DSA_BF16 ? kPathBF16 : kPathFP8;
     return DSA_OK;
   }
@@ -116,7 +117,7 @@ AttnLaunch make_attn(const dsa_problem_t& p, const void* qa, const void* kv, con
   a.part_o = nullptr; a.part_lse = nullptr;
   if (splits > 1) {
     const int rows = p.batch * q_count;
-    a.part_o = static_cast<float*>(part);
+    a.part_o = part;
     a.part_lse = reinterpret_cast<float*>(static_cast<char*>(part) +
                                           align_up((size_t)rows * splits * p.attn_heads * p.v_dim * 4));
   }

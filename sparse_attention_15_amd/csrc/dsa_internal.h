@@ -37,7 +37,8 @@ struct AttnLaunch {
   const int32_t* idx;      // [B][Lq][K] (full-tensor numbering)
   void* out;               // [B][Lq][NH][Dv]
   float* lse;              // [B][Lq][NH] or null
-  float* part_o;           // split partials [rows][S][NH][Dv] fp32 (S > 1 only)
+  void* part_o;            // split partials [rows][S][NH][Dv] (S > 1 only), in the
+                           // output's precision: fp32 for fp32 out, bf16 for bf16 out
   float* part_lse;         // [rows][S][NH]
   int B, Lq, Lk, NH, Dqk, Dv, K;
   int q_begin, q_count;

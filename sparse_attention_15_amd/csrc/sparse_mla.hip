@@ -68,18 +68,29 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | (((N >> 4) & 3) << 14));
 }
 
-// 16-byte global -> LDS copy per lane (LDS destination = lds_base + 16*lane).
-// Written as asm so that the compiler's wait-count pass does not treat the
-// in-flight copies into other stage buffers as hazards for the current one;
-// completion is awaited explicitly with wait_vmcnt<>().  The instruction has
-// no register outputs.
-// M0 is reserved by the compiler (gfx9 LDS instructions do not read it and
-// nothing else in these kernels uses it); it is named as clobbered anyway.
+// 16-byte global -> LDS copy per lane (LDS destination = lds_base + 16*lane,
+// global source = gbase + row_off + (map >> 8)).  Written as asm so that the
+// compiler's wait-count pass does not treat the in-flight copies into other
+// stage buffers as hazards for the current one; completion is awaited
+// explicitly with wait_vmcnt<>().  The address add sits inside the asm so
+// that the LDS read of row_off is only waited for here.  No memory clobber:
+// the copies only target a stage buffer that nothing reads before the next
+// barrier, and the asm stays ordered after that barrier (both are volatile
+// asm).  An SALU write of M0 needs one wait state before an LDS-DMA reads it.
+// M0 is named as clobbered (nothing else in these kernels uses it).
 #pragma clang diagnostic push
 #pragma clang diagnostic ignored "-Winline-asm"
-__device__ __forceinline__ void dma16(const void* gbase, uint32_t voff, uint32_t lds_base) {
-  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(lds_base), "v"(voff), "s"(gbase)
-               : "memory", "m0");
+__device__ __forceinline__ void dma16(const void* gbase, uint32_t row_off, uint32_t map, uint32_t lds_base) {
+  uint32_t t;
+  asm volatile(
+      "v_lshrrev_b32 %0, 8, %2\n\t"
+      "v_add_u32 %0, %0, %1\n\t"
+      "s_mov_b32 m0, %3\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %0, %4"
+      : "=&v"(t)
+      : "v"(row_off), "v"(map), "s"(lds_base), "s"(gbase)
+      : "m0");
 }
 #pragma clang diagnostic pop
 
@@ -100,20 +111,16 @@ __device__ __forceinline__ u32x2 tr_read(const uint8_t* p) {
   return __builtin_bit_cast(u32x2, v);
 }
 
-// Work split: 8 waves = 4 pairs; pair p owns heads 32p .. 32p+31 and the two
-// partners split the work, per 32-key block, on 32x32x16 MFMA:
-//   QK: partner d computes the partial S^T over dims [288d, 288d + 288)
-//       (18 k-steps; its Q^T fragments stay in 72 registers), writes it to
-//       LDS, and after a barrier adds the other partner's partial, so both
-//       hold the same full S^T (fp32 addition commutes);
-//   softmax: done identically by both partners;
-//   PV: partner d accumulates O^T for value dims [256d, 256d + 256).
-// Lane l: column = head 32p + (l % 32), half hf = l / 32.
+// Work split: 4 waves, one per SIMD, so each wave has the whole register
+// file of its SIMD (512 registers: the O accumulators live in AGPRs).  Wave w
+// owns heads 32w .. 32w+31 for all 576 dims and all 512 value dims, on
+// 32x32x16 MFMA, so no partial scores cross waves.
+// Lane l: column = head 32w + (l % 32), half hf = l / 32.
 //   S^T rows (keys) held: 8q + 4hf + r, q, r = 0..3.
-//   O^T rows (value dims) held: 256d + 32vt + 8q + 4hf + r.
-constexpr int kWavesA = 8;
-constexpr int kQSteps = 18;                      // 16-dim k-steps per partner
-constexpr int kVTiles = 8;                       // 32-wide value tiles per partner
+//   O^T rows (value dims) held: 32vt + 8q + 4hf + r, vt = 0..15.
+constexpr int kWavesA = 4;
+constexpr int kQSteps = kDqk / 16;               // 36 k-steps of 16 dims
+constexpr int kVTiles = kDv / 32;                // 16 value tiles of 32 dims
 struct AttnState {
   u32x4 qf[kQSteps];   // Q^T fragments (B operand)
   f32x16 o[kVTiles];   // O^T accumulators
@@ -121,35 +128,95 @@ struct AttnState {
 };
 
 // Gather instructions per wave per block: 38 x 64-lane 16-byte copies
-// split 5,5,5,5,5,5,4,4 over the 8 waves.
-__device__ __forceinline__ int dma_first(int wave) { return wave < 6 ? 5 * wave : 30 + 4 * (wave - 6); }
+// split 10, 10, 9, 9 over the 4 waves.
+constexpr int kDmaMax = 10;
+__device__ __forceinline__ int dma_first(int wave) { return wave < 2 ? 10 * wave : 20 + 9 * (wave - 2); }
 static_assert(kDmaInstr == 38, "gather split assumes 38 instructions per block");
 
+// QK MFMAs with the accumulator in VGPRs.  The kernel's builtin MFMAs (PV)
+// are selected in AGPR form, which puts the 256-register O accumulator in the
+// AGPR file; writing the QK chain as asm keeps S (and Q) in VGPRs instead of
+// a second AGPR tile.  Back-to-back accumulation into the same registers
+// needs no wait states; the last step of the chain waits out the result
+// latency before any VALU instruction reads S (24 wait states, more than the
+// 8-pass MFMA needs).
+__device__ __forceinline__ void qk_first(f32x16& d, const u32x4& a, const u32x4& b) {
+  asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(d) : "v"(a), "v"(b));
+}
+__device__ __forceinline__ void qk_next(f32x16& d, const u32x4& a, const u32x4& b) {
+  asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(d) : "v"(a), "v"(b));
+}
+__device__ __forceinline__ void qk_last(f32x16& d, const u32x4& a, const u32x4& b) {
+  asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(d) : "v"(a), "v"(b));
+}
+
+__device__ __forceinline__ void scale_tile(f32x16& o, float alpha) {
+  float e[16];
+#pragma unroll
+  for (int k = 0; k < 16; ++k) e[k] = o[k];
+  float t;
+  asm volatile(
+      "s_nop 7\n\ts_nop 7\n\ts_nop 7\n\t"
+#define R(k) "v_accvgpr_read_b32 %16, %" #k "\n\tv_mul_f32 %16, %17, %16\n\tv_accvgpr_write_b32 %" #k ", %16\n\t"
+      R(0) R(1) R(2) R(3) R(4) R(5) R(6) R(7) R(8) R(9) R(10) R(11) R(12) R(13) R(14) R(15)
+#undef R
+      "s_nop 4"
+      : "+a"(e[0]), "+a"(e[1]), "+a"(e[2]), "+a"(e[3]), "+a"(e[4]), "+a"(e[5]), "+a"(e[6]), "+a"(e[7]),
+        "+a"(e[8]), "+a"(e[9]), "+a"(e[10]), "+a"(e[11]), "+a"(e[12]), "+a"(e[13]), "+a"(e[14]), "+a"(e[15]),
+        "=&v"(t)
+      : "v"(alpha));
+#pragma unroll
+  for (int k = 0; k < 16; ++k) o[k] = e[k];
+}
+
+// Row gathers of a later block, issued from inside the QK chain of the
+// current one so that their address and issue latency overlaps the MFMAs.
+struct Gather {
+  const uint8_t* kvb;     // this sequence's latent rows (wave-uniform)
+  const uint32_t* bp;     // LDS row byte offsets of the block to gather
+  uint32_t dst;           // LDS stage buffer of that block
+  int dfirst, dcount;     // this wave's gather instructions
+  bool active;            // wave-uniform: is there a block to gather
+};
+
 // One 32-row block.
-__device__ __forceinline__ void attn_block(AttnState& st, const uint8_t* buf, uint32_t vmask, float* exch_mine,
-                                           const float* exch_other, const int (&qk_off)[2],
-                                           const int (&pv_off)[2][2], int hf, float zscale) {
+__device__ __forceinline__ void attn_block(AttnState& st, const uint8_t* buf, uint32_t vmask,
+                                           const int (&qk_off)[2], const int (&pv_off)[2][2], int hf,
+                                           float zscale, const Gather& g, const uint32_t (&dma_map)[kDmaMax]) {
+  // gather instruction k: its row positions are read from LDS after QK step
+  // 3k - 1 and the copy is issued after step 3k + 1, so the LDS latency
+  // of the position read hides behind two MFMAs
+  // gather instruction k: the row's byte offset is read from LDS after QK
+  // step 3k - 1 and the copy is issued after step 3k + 1
+  uint32_t roff[kDmaMax];
+  auto addr = [&](int k) {
+    uint32_t m = dma_map[k];
+    asm("" : "+v"(m));                          // keep the packed form (one register)
+    roff[k] = g.bp[m & 0xffu];
+  };
+  if (g.active) addr(0);
+  // A operands: a ring of kRing LDS reads in flight ahead of the MFMAs
+  constexpr int kRing = 4;
+  u32x4 av[kRing];
+#pragma unroll
+  for (int t = 0; t < kRing; ++t) av[t] = ld16(buf + qk_off[t & 1] + 64 * (t >> 1));
   f32x16 s;
 #pragma unroll
-  for (int e = 0; e < 16; ++e) s[e] = 0.f;
-#pragma unroll
-  for (int t = 0; t < kQSteps; ++t) s = mfma32(ld16(buf + qk_off[t & 1] + 64 * (t >> 1)), st.qf[t], s);
-  // exchange partial scores with the partner wave (lane-linear, 4 x 16 B)
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const f32x4 v = {s[4 * q], s[4 * q + 1], s[4 * q + 2], s[4 * q + 3]};
-    *reinterpret_cast<f32x4*>(exch_mine + q * 256) = v;
-  }
-  __builtin_amdgcn_s_waitcnt(0xc07f);             // lgkmcnt(0)
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const f32x4 v = *reinterpret_cast<const f32x4*>(exch_other + q * 256);
-    s[4 * q] += v[0];
-    s[4 * q + 1] += v[1];
-    s[4 * q + 2] += v[2];
-    s[4 * q + 3] += v[3];
+  for (int t = 0; t < kQSteps; ++t) {
+    const u32x4 a_t = av[t % kRing];
+    if (t + kRing < kQSteps) av[t % kRing] = ld16(buf + qk_off[(t + kRing) & 1] + 64 * ((t + kRing) >> 1));
+    if (t == 0) qk_first(s, a_t, st.qf[t]);
+    else if (t == kQSteps - 1) qk_last(s, a_t, st.qf[t]);
+    else qk_next(s, a_t, st.qf[t]);
+    if (t % 3 == 2 && t / 3 + 1 < kDmaMax) {
+      const int k = t / 3 + 1;
+      if (g.active && k < g.dcount) addr(k);
+    }
+    if (t % 3 == 1 && t / 3 < kDmaMax) {
+      const int k = t / 3;
+      if (g.active && k < g.dcount)
+        dma16(g.kvb, roff[k], dma_map[k], __builtin_amdgcn_readfirstlane(g.dst + (g.dfirst + k) * 1024));
+    }
   }
   // scaled base-2 logits; keys not listed in this block (bit clear in
   // vmask) get -inf.  This lane's keys: 8q + 4hf + r.
@@ -169,10 +236,12 @@ __device__ __forceinline__ void attn_block(AttnState& st, const uint8_t* buf, ui
   mb = max_xor32(mb);
   if (__ballot(mb > st.m_run + kTau)) {
     const float m_new = fmaxf(st.m_run, mb);
-    const float alpha = (st.m_run == kNegInf) ? 0.f : __builtin_amdgcn_exp2f(st.m_run - m_new);
+    if (__ballot(st.m_run != kNegInf)) {          // before the first raise O and l are zero
+      const float alpha = (st.m_run == kNegInf) ? 0.f : __builtin_amdgcn_exp2f(st.m_run - m_new);
 #pragma unroll
-    for (int v = 0; v < kVTiles; ++v) st.o[v] *= alpha;
-    st.l_run *= alpha;
+      for (int v = 0; v < kVTiles; ++v) scale_tile(st.o[v], alpha);
+      st.l_run *= alpha;
+    }
     st.m_run = m_new;
   }
   const float mref = (st.m_run == kNegInf) ? 0.f : st.m_run;
@@ -205,14 +274,12 @@ __device__ __forceinline__ void attn_block(AttnState& st, const uint8_t* buf, ui
 
 __global__ __launch_bounds__(kWavesA * 64, 1) void attn_bf16_kernel(AttnLaunch a) {
   __shared__ __attribute__((aligned(16))) uint8_t stg[3 * kStageBytes];
-  __shared__ __attribute__((aligned(16))) int spos[kMaxPer];
+  __shared__ __attribute__((aligned(16))) uint32_t spos[kMaxPer];
   __shared__ uint32_t bmask[kMaxPer / kBK];       // per 32-entry block: bit j = entry j usable
-  __shared__ __attribute__((aligned(16))) float exch[kWavesA * 1024];   // 4 KiB of partial scores per wave
-  __shared__ int s_last;
+  __shared__ int s_lastw[kWavesA];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int hf = lane >> 5, c32 = lane & 31;
-  const int pair = wave >> 1, d = wave & 1;
   const int split = blockIdx.x;
   const int rr = gridDim.y - 1 - blockIdx.y;    // launch row; latest queries first
   const int b = rr / a.q_count;
@@ -222,26 +289,45 @@ __global__ __launch_bounds__(kWavesA * 64, 1) void attn_bf16_kernel(AttnLaunch a
   const int j0 = split * per;
   const int nent = max(0, min(a.K, j0 + per) - j0);
 
-  // Chosen positions of this split into LDS (-1 for skipped / padding).
-  if (tid == 0) s_last = -1;
-  __syncthreads();
-  int my_last = -1;
+  // This split's list entries (all loads in flight at once), then the Q
+  // fragments; vector-memory completion is in order, so the list can be
+  // processed while the Q loads are still arriving.
+  constexpr int kFillIt = kMaxPer / (kWavesA * 64);
+  int pv[kFillIt];
   const int32_t* idx = a.idx + qrow * a.K + j0;
-  for (int j = tid; j < per; j += kWavesA * 64) {
-    int pos = j < nent ? idx[j] : -1;
-    if (pos >= a.Lk) pos = -1;
-    spos[j] = pos < 0 ? -1 : pos;
-    if (pos >= 0) my_last = j;
+#pragma unroll
+  for (int it = 0; it < kFillIt; ++it) {
+    const int j = (it * kWavesA + wave) * 64 + lane;
+    pv[it] = j < nent ? idx[j] : -1;
   }
-  if (my_last >= 0) atomicMax(&s_last, my_last);
-
   AttnState st;
-  const int h = 32 * pair + c32;
+  const int h = 32 * wave + c32;
   {
-    const uint8_t* qb = static_cast<const uint8_t*>(a.qa) + (qrow * kNH + h) * (int64_t)kRowB + 576 * d;
+    const uint8_t* qb = static_cast<const uint8_t*>(a.qa) + (qrow * kNH + h) * (int64_t)kRowB;
 #pragma unroll
     for (int t = 0; t < kQSteps; ++t) st.qf[t] = ld16(qb + (16 * t + 8 * hf) * 2);
   }
+  // Chosen rows into LDS as byte offsets (row * 1152; skipped and padding
+  // entries point at row 0), one validity bit per entry in bmask (bit j of
+  // word w: entry 32w + j is usable), and each wave's last usable entry.
+  int my_last = -1;
+#pragma unroll
+  for (int it = 0; it < kFillIt; ++it) {
+    const int jw = (it * kWavesA + wave) * 64;
+    if (jw < per) {
+      int pos = pv[it];
+      if (pos >= a.Lk) pos = -1;
+      const uint64_t bal = __ballot(pos >= 0);
+      spos[jw + lane] = (uint32_t)max(pos, 0) * kRowB;
+      if (lane == 0) {
+        bmask[jw / kBK] = (uint32_t)bal;
+        if (jw + kBK < per) bmask[jw / kBK + 1] = (uint32_t)(bal >> 32);
+      }
+      if (bal) my_last = jw + 63 - __builtin_clzll(bal);
+    }
+  }
+  if (lane == 0) s_lastw[wave] = my_last;
+
 #pragma unroll
   for (int v = 0; v < kVTiles; ++v)
 #pragma unroll
@@ -250,20 +336,20 @@ __global__ __launch_bounds__(kWavesA * 64, 1) void attn_bf16_kernel(AttnLaunch a
   st.l_run = 0.f;
   const float zscale = a.scale * kLog2e;
 
-  // QK operand: key row c32, logical chunk 36d + 2t + hf
-  //   = 36d + 4(t >> 1) + (2(t & 1) + hf), stored with the low two bits
+  // QK operand: key row c32, logical chunk 2t + hf
+  //   = 4(t >> 1) + (2(t & 1) + hf), stored with the low two bits
   //   XOR swz(row): offset qk_off[t & 1] + 64 * (t >> 1).
   int qk_off[2];
   {
     const int f = swz(c32);
 #pragma unroll
-    for (int par = 0; par < 2; ++par) qk_off[par] = c32 * kLdsRow + 576 * d + 16 * ((2 * par + hf) ^ f);
+    for (int par = 0; par < 2; ++par) qk_off[par] = c32 * kLdsRow + 16 * ((2 * par + hf) ^ f);
   }
   // PV operand (transposed reads) for 32x32x16: 16-lane group G holds value
   // rows 16(G&1) + j of the tile and k-half G>>1.  Step k, part w (lo/hi)
   // reads key row 16k + 8w + 4(G>>1) + j/4, value columns
-  // 256d + 32vt + 16(G&1) + 4(j&3) .. +3: logical chunk 32d + 4vt + k0 with
-  // k0 = 2(G&1) + (j&3)/2, byte (j&1)*8; stored at 32d + 4vt + (k0 ^ swz):
+  // 32vt + 16(G&1) + 4(j&3) .. +3: logical chunk 4vt + k0 with
+  // k0 = 2(G&1) + (j&3)/2, byte (j&1)*8; stored at 4vt + (k0 ^ swz):
   // offset pv_off[k][w] + 64 * vt.
   int pv_off[2][2];
   {
@@ -274,86 +360,81 @@ __global__ __launch_bounds__(kWavesA * 64, 1) void attn_bf16_kernel(AttnLaunch a
 #pragma unroll
       for (int w = 0; w < 2; ++w) {
         const int row = 16 * k + 8 * w + 4 * (G >> 1) + (j >> 2);
-        pv_off[k][w] = row * kLdsRow + 16 * (32 * d + (k0 ^ swz(row))) + within;
+        pv_off[k][w] = row * kLdsRow + 16 * (k0 ^ swz(row)) + within;
       }
   }
   __syncthreads();
-  const int nblk = (s_last + kBK) / kBK;          // blocks up to the last listed entry
+  const int last = max(max(s_lastw[0], s_lastw[1]), max(s_lastw[2], s_lastw[3]));
+  const int nblk = (last + kBK) / kBK;            // blocks up to the last listed entry
   // Consume the Q fragments here so that their loads are complete before the
   // loop: the compiler's own vector-memory waits would otherwise stay inside
   // the loop and also stall on the in-flight row gathers.
 #pragma unroll
   for (int t = 0; t < kQSteps; ++t) asm volatile("" : "+v"(st.qf[t]));
-  for (int blk = wave; blk < nblk; blk += kWavesA) {
-    const uint64_t bal = __ballot(lane < kBK && spos[blk * kBK + (lane & (kBK - 1))] >= 0);
-    if (lane == 0) bmask[blk] = (uint32_t)bal;
-  }
-  __syncthreads();
 
   // Gather map: instruction k of this wave fills LDS chunk slots
-  // f = (dma_first(wave) + k)*64 + lane: row f/76, stored chunk f%76 (slots
-  // 72..75 are padding and stay unloaded), which holds logical chunk
-  // (f%76) ^ swz(row).
+  // f = (dma_first(wave) + k)*64 + lane: row f/76, stored chunk f%76, which
+  // holds logical chunk (f%76) ^ swz(row).  Slots 72..75 of a row are
+  // padding that no operand read touches; their lanes copy the row's first
+  // chunk there (same cache line as a real copy), so every lane of a gather
+  // instruction is active and the addressing has no branches.
   const int dfirst = dma_first(wave);
-  const int dcount = wave < 6 ? 5 : 4;
-  // per lane and gather instruction: row (low 8 bits) | stored-chunk byte
-  // offset << 8, or ~0u for a padding slot
-  uint32_t dma_map[5];
+  const int dcount = wave < 2 ? 10 : 9;
+  // per lane and gather instruction: row (low 8 bits) | global byte offset
+  // within the row << 8
+  uint32_t dma_map[kDmaMax];
 #pragma unroll
-  for (int k = 0; k < 5; ++k) {
+  for (int k = 0; k < kDmaMax; ++k) {
     const int f = (dfirst + k) * 64 + lane;
     const int r = f / kLdsChunks, p = f - r * kLdsChunks;
-    dma_map[k] = p < kChunks ? ((uint32_t)r | ((uint32_t)((p ^ swz(r)) << 4) << 8)) : ~0u;
+    dma_map[k] = k >= dcount ? 0u : ((uint32_t)r | ((uint32_t)(p < kChunks ? (p ^ swz(r)) << 4 : 0) << 8));
   }
   const uint8_t* kvb = static_cast<const uint8_t*>(a.kv) + (int64_t)b * a.Lk * kRowB;   // uniform
   const uint32_t stg_lds = lds_addr(stg);
   auto issue = [&](int blk, int sb) {
     const uint32_t dst = __builtin_amdgcn_readfirstlane(stg_lds + sb * kStageBytes);
-    const int* bp = spos + blk * kBK;
-    uint32_t voff[5];
+    const uint32_t* bp = spos + blk * kBK;
+    uint32_t roff[kDmaMax];
 #pragma unroll
-    for (int k = 0; k < 5; ++k) {               // all position reads first: one LDS latency
-      uint32_t m = dma_map[k];
-      asm volatile("" : "+v"(m));               // keep the packed form (one register)
-      voff[k] = m == ~0u ? ~0u : (uint32_t)max(bp[m & 0xffu], 0) * kRowB + (m >> 8);
-    }
+    for (int k = 0; k < kDmaMax; ++k) roff[k] = bp[dma_map[k] & 0xffu];
 #pragma unroll
-    for (int k = 0; k < 5; ++k) {
-      if (k < dcount) {
-        const uint32_t ldst = __builtin_amdgcn_readfirstlane(dst + (dfirst + k) * 1024);
-        if (voff[k] != ~0u) dma16(kvb, voff[k], ldst);
-      }
-    }
+    for (int k = 0; k < kDmaMax; ++k)
+      if (k < dcount) dma16(kvb, roff[k], dma_map[k], __builtin_amdgcn_readfirstlane(dst + (dfirst + k) * 1024));
   };
-  float* exch_mine = exch + wave * 1024 + lane * 4;
-  const float* exch_other = exch + (wave ^ 1) * 1024 + lane * 4;
   // Block blk lives in stage buffer blk % 3.  Wait for its gather (the next
-  // block's may stay in flight), barrier (every wave is then also done with
-  // block blk-1's buffer and scores exchange), start the gather two blocks
-  // ahead into that buffer, then compute.
+  // block's may stay in flight) and barrier: every wave is then also done with
+  // block blk-1, whose buffer receives block blk+2, gathered from inside
+  // block blk's QK steps.
   if (nblk > 0) issue(0, 0);
   if (nblk > 1) issue(1, 1);
   int sb = 0;
+  Gather g;
+  g.kvb = kvb;
+  g.dfirst = dfirst;
+  g.dcount = dcount;
   for (int blk = 0; blk < nblk; ++blk) {
     if (blk + 1 < nblk) {
-      if (dcount == 5) wait_vmcnt<5>();
-      else wait_vmcnt<4>();
+      if (dcount == 10) wait_vmcnt<10>();
+      else wait_vmcnt<9>();
     } else {
       wait_vmcnt<0>();
     }
     __builtin_amdgcn_s_waitcnt(0xc07f);           // lgkmcnt(0)
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
-    if (blk + 2 < nblk) issue(blk + 2, sb == 0 ? 2 : sb - 1);
+    const int sn = sb == 0 ? 2 : sb - 1;          // buffer of blocks blk-1 and blk+2
+    g.active = blk + 2 < nblk;
+    g.bp = spos + (blk + 2) * kBK;
+    g.dst = __builtin_amdgcn_readfirstlane(stg_lds + sn * kStageBytes);
     const uint32_t vmask = __builtin_amdgcn_readfirstlane(bmask[blk]);
-    attn_block(st, stg + sb * kStageBytes, vmask, exch_mine, exch_other, qk_off, pv_off, hf, zscale);
+    attn_block(st, stg + sb * kStageBytes, vmask, qk_off, pv_off, hf, zscale, g, dma_map);
     sb = sb == 2 ? 0 : sb + 1;
   }
 
   const float l_tot = st.l_run + shfl_xor(st.l_run, 32);
   const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
   const float lse = l_tot > 0.f ? (st.m_run + log2f(l_tot)) * kLn2 : kNegInf;
-  const int vbase = 256 * d + 4 * hf;
+  const int vbase = 4 * hf;
   if (a.splits == 1) {
     if (a.out_f32) {
       float* op = static_cast<float*>(a.out) + (qrow * kNH + h) * kDv + vbase;
@@ -376,24 +457,36 @@ __global__ __launch_bounds__(kWavesA * 64, 1) void attn_bf16_kernel(AttnLaunch a
           *reinterpret_cast<u32x2*>(op + 32 * vt + 8 * q) = v2;
         }
     }
-    if (a.lse && hf == 0 && d == 0) a.lse[qrow * kNH + h] = lse;
+    if (a.lse && hf == 0) a.lse[qrow * kNH + h] = lse;
   } else {
     const int64_t prow = (int64_t)rr * a.splits + split;
-    float* op = a.part_o + (prow * kNH + h) * kDv + vbase;
+    if (a.out_f32) {
+      float* op = static_cast<float*>(a.part_o) + (prow * kNH + h) * kDv + vbase;
 #pragma unroll
-    for (int vt = 0; vt < kVTiles; ++vt)
+      for (int vt = 0; vt < kVTiles; ++vt)
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const f32x4 v4 = {st.o[vt][4 * q] * inv, st.o[vt][4 * q + 1] * inv, st.o[vt][4 * q + 2] * inv,
-                          st.o[vt][4 * q + 3] * inv};
-        *reinterpret_cast<f32x4*>(op + 32 * vt + 8 * q) = v4;
-      }
-    if (hf == 0 && d == 0) a.part_lse[prow * kNH + h] = lse;
+        for (int q = 0; q < 4; ++q) {
+          const f32x4 v4 = {st.o[vt][4 * q] * inv, st.o[vt][4 * q + 1] * inv, st.o[vt][4 * q + 2] * inv,
+                            st.o[vt][4 * q + 3] * inv};
+          *reinterpret_cast<f32x4*>(op + 32 * vt + 8 * q) = v4;
+        }
+    } else {
+      uint16_t* op = static_cast<uint16_t*>(a.part_o) + (prow * kNH + h) * kDv + vbase;
+#pragma unroll
+      for (int vt = 0; vt < kVTiles; ++vt)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const u32x2 v2 = {pack_bf16x2(st.o[vt][4 * q] * inv, st.o[vt][4 * q + 1] * inv),
+                            pack_bf16x2(st.o[vt][4 * q + 2] * inv, st.o[vt][4 * q + 3] * inv)};
+          *reinterpret_cast<u32x2*>(op + 32 * vt + 8 * q) = v2;
+        }
+    }
+    if (hf == 0) a.part_lse[prow * kNH + h] = lse;
   }
 }
 
 // Merge split partials: out = sum_s exp(lse_s - LSE) * O_s, LSE = log sum_s exp(lse_s).
-// grid (NH, rows), Dv/4 threads.
+// grid (NH, rows), Dv/4 threads; partials in the output's precision.
 __global__ __launch_bounds__(256) void attn_combine_kernel(AttnLaunch a) {
   const int h = blockIdx.x, rr = blockIdx.y, v = threadIdx.x * 4;
   const int S = a.splits, NH = a.NH, Dv = a.Dv;
@@ -411,7 +504,14 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnLaunch a) {
       if (ls == kNegInf) continue;
       const float wgt = __expf(ls - m);
       sum += wgt;
-      const f32x4 po = *reinterpret_cast<const f32x4*>(a.part_o + (((int64_t)rr * S + s) * NH + h) * Dv + v);
+      const int64_t off = (((int64_t)rr * S + s) * NH + h) * Dv + v;
+      f32x4 po;
+      if (a.out_f32) {
+        po = *reinterpret_cast<const f32x4*>(static_cast<const float*>(a.part_o) + off);
+      } else {
+        const u32x2 pb = *reinterpret_cast<const u32x2*>(static_cast<const uint16_t*>(a.part_o) + off);
+        po = f32x4{bf16_lo(pb[0]), bf16_hi(pb[0]), bf16_lo(pb[1]), bf16_hi(pb[1])};
+      }
       acc += wgt * po;
     }
     acc *= 1.f / sum;
