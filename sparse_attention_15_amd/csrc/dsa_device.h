@@ -67,6 +67,33 @@ __device__ __forceinline__ float wave_sum(float v) {
   return v;
 }
 
+// s_waitcnt on the vector-memory counter only (gfx9 encoding: expcnt and
+// lgkmcnt fields left at their maxima).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | (((N >> 4) & 3) << 14));
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) uint8_t*)(p);
+}
+
+// 16-byte global -> LDS copy per lane: lane l's 16 bytes at gbase + voff go
+// to LDS address lds_base + 16*l.  Written as asm so that the compiler's
+// wait-count pass does not treat in-flight copies as hazards for unrelated
+// LDS reads; callers await completion with wait_vmcnt<>() (and a barrier
+// when other waves read the data).  An SALU write of M0 needs one wait state
+// before an LDS-DMA reads it.  No memory clobber: callers order the copies
+// against readers of the destination with their own waits and barriers.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void lds_dma16(const void* gbase, uint32_t voff, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2 nt"
+               ::"s"(lds_base), "v"(voff), "s"(gbase)
+               : "m0");
+}
+#pragma clang diagnostic pop
+
 // ue8m0 exponent byte -> 2^(e-127) as fp32 (e = 0 gives 2^-127, a subnormal).
 __device__ __forceinline__ float ue8m0_to_f32(uint32_t e) {
   return e == 0 ? __builtin_bit_cast(float, 0x00400000u) : __builtin_bit_cast(float, e << 23);

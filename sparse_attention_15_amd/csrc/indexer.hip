@@ -11,9 +11,10 @@
 // bf16 / fp8 kernels (H = 64, D = 128): the per-head dot products are an MFMA
 // GEMM with heads on the M axis (4 tiles of 16) and keys on the N axis, so
 // the ReLU-weighted head reduction happens in registers: 16 values per lane,
-// then two cross-lane adds.  Keys are read once per query group: straight
-// from HBM into registers for decode-shaped launches, through a swizzled,
-// double-buffered LDS tile shared by 8 queries for prefill-shaped ones.
+// then two cross-lane adds.  Keys are read once per query group: through a
+// per-wave LDS-DMA ring of whole key rows for decode-shaped launches, through
+// a swizzled, double-buffered LDS tile shared by 8 queries for prefill-shaped
+// ones.
 // FP8 (E4M3 codes + ue8m0 row scales): the MFMA consumes raw codes; the
 // query-row scales fold into the head weights and the key scale multiplies
 // the head sum.  Both are powers of two and ReLU is positively homogeneous,
@@ -158,55 +159,108 @@ __device__ __forceinline__ float tile_score(const QFrag<FP8>& q, const KFrag<FP8
 }
 
 // ------------------------------------------------------ decode shape -------
-// grid (ceil(Lk / chunk), B * q_count), 4 waves; wave w streams keys
-// [c0 + w*chunk/4, c0 + (w+1)*chunk/4) of its query in 64-key steps, with
-// the next step's loads in flight while the current step computes.
+// grid (ceil(Lk / 2048), B * q_count), 4 waves; wave w owns keys
+// [c0 + 512w, c0 + 512w + 512) of its query.  Keys stream through a private
+// 4-stage LDS ring of 16-key tiles filled by LDS-DMA (global_load_lds): each
+// copy instruction moves whole 256-byte (bf16) or 128-byte (fp8) key rows, so
+// every request is a full cache line, and no registers hold data in flight.
+// Within a staged row the 16-byte chunks are XOR-permuted by the row index,
+// which makes the MFMA operand reads conflict-free.  Scores collect in LDS
+// and leave with one coalesced store per wave, so the vector-memory counter
+// only tracks the copies.
+constexpr int kDecChunk = 2048;                  // keys per work-group
+constexpr int kDecPerWave = kDecChunk / 4;
+constexpr int kDecRing = 4;
+
 template <bool FP8>
-__global__ __launch_bounds__(256, 2) void idx_decode_kernel(IndexLaunch a, int chunk) {
+__global__ __launch_bounds__(256, 2) void idx_decode_kernel(IndexLaunch a) {
+  constexpr int ROWB = FP8 ? kD : 2 * kD;        // bytes per key row
+  constexpr int CPR = ROWB / 16;                 // 16-byte chunks per row
+  constexpr int TK = 16;                         // keys per stage
+  constexpr int STG = TK * ROWB;                 // bytes per stage
+  constexpr int NDMA = STG / 1024;               // copy instructions per stage
+  __shared__ __attribute__((aligned(16))) uint8_t ring[4][kDecRing][STG];
+  __shared__ __attribute__((aligned(16))) float sc[4][kDecPerWave];
+  __shared__ __attribute__((aligned(16))) uint8_t kscale[4][FP8 ? kDecPerWave : 16];
+
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int row = blockIdx.y;
   const int b = row / a.q_count;
   const int i = a.q_begin + row % a.q_count;
   const int n = a.Lk - a.Lq + i + 1;
-  const int per_wave = chunk >> 2;
-  const int w0 = blockIdx.x * chunk + wave * per_wave;
-  const int w1 = min(w0 + per_wave, a.Lk);
+  const int w0 = blockIdx.x * kDecChunk + wave * kDecPerWave;
+  const int w1 = min(w0 + kDecPerWave, a.Lk);
   const int wn = min(w1, n);
   float* out = a.scores + (int64_t)row * a.row_stride;
-  if (a.write_masked)
+  if (a.write_masked) {
     for (int s = max(w0, n) + lane; s < w1; s += 64) out[s] = kNegInf;
+    wait_vmcnt<0>();
+  }
   if (w0 >= wn) return;
+  const int nk = wn - w0;
+  const int nst = (nk + TK - 1) / TK;
 
   const int64_t qrow = (int64_t)b * a.Lq + i;
+  const uint8_t* kbase = static_cast<const uint8_t*>(a.k) + (int64_t)b * a.Lk * ROWB;   // wave-uniform
+  if constexpr (FP8) {
+    const uint8_t* ks = a.k_scale + (int64_t)b * a.Lk;
+    for (int j = lane; j < nk; j += 64) kscale[wave][j] = ks[w0 + j];
+  }
   QFrag<FP8> q;
   float wv[16];
   load_query<FP8>(a, qrow, lane, q, wv);
-  const uint8_t* kbase = static_cast<const uint8_t*>(a.k) + (int64_t)b * a.Lk * (FP8 ? kD : 2 * kD);
-  const uint8_t* ks = FP8 ? a.k_scale + (int64_t)b * a.Lk : nullptr;
+  wait_vmcnt<0>();                               // from here on only the copies use the counter
 
-  KFrag<FP8> cur[4], nxt[4];
+  // copy k of a stage fills LDS slots 64k + lane: row slot/CPR, stored
+  // position slot%CPR, holding global chunk position ^ (row % CPR)
+  int drow[NDMA], dchk[NDMA];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) load_keys_global<FP8>(kbase, w0 + 16 * j, a.Lk, lane, cur[j]);
-  for (int k0 = w0; k0 < wn; k0 += 64) {
-    const bool more = k0 + 64 < wn;
-    if (more) {
+  for (int k = 0; k < NDMA; ++k) {
+    const int slot = 64 * k + lane;
+    drow[k] = slot / CPR;
+    dchk[k] = (slot % CPR) ^ (drow[k] & (CPR - 1));
+  }
+  const uint32_t ring_lds = lds_addr(&ring[wave][0][0]);
+  auto issue = [&](int st) {
+    const int k0 = w0 + st * TK;
+    const uint32_t dst = __builtin_amdgcn_readfirstlane(ring_lds + (st % kDecRing) * STG);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) load_keys_global<FP8>(kbase, k0 + 64 + 16 * j, a.Lk, lane, nxt[j]);
+    for (int k = 0; k < NDMA; ++k) {
+      const int key = min(k0 + drow[k], a.Lk - 1);   // rows past the end repeat the last key
+      lds_dma16(kbase, (uint32_t)key * ROWB + dchk[k] * 16, dst + 1024 * k);
     }
+  };
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      float s = tile_score<FP8>(q, cur[j], wv);
-      const int key = k0 + 16 * j + lane;
-      if constexpr (FP8) {
-        if (lane < 16 && key < wn) s *= ue8m0_to_f32(ks[key]);
-      }
-      if (lane < 16 && key < wn) out[key] = s;
+  for (int st = 0; st < kDecRing - 1; ++st)
+    if (st < nst) issue(st);
+
+  const int r16 = lane & 15, g = lane >> 4;
+  for (int st = 0; st < nst; ++st) {
+    // stage st is complete when at most the later in-flight stages remain
+    if (st + 2 < nst) wait_vmcnt<2 * NDMA>();
+    else if (st + 1 < nst) wait_vmcnt<NDMA>();
+    else wait_vmcnt<0>();
+    asm volatile("" ::: "memory");
+    // the slot of stage st-1 is free again (its reads have returned)
+    if (st + kDecRing - 1 < nst) issue(st + kDecRing - 1);
+    const uint8_t* lrow = &ring[wave][st % kDecRing][r16 * ROWB];
+    KFrag<FP8> kf;
+    if constexpr (!FP8) {
+#pragma unroll
+      for (int t = 0; t < 4; ++t) kf.v[t] = ld16(lrow + (((4 * t + g) ^ r16) * 16));
+    } else {
+      kf.v = join(ld16(lrow + (((2 * g) ^ (r16 & 7)) * 16)), ld16(lrow + (((2 * g + 1) ^ (r16 & 7)) * 16)));
     }
-    if (more) {
-#pragma unroll
-      for (int j = 0; j < 4; ++j) cur[j] = nxt[j];
+    float s = tile_score<FP8>(q, kf, wv);
+    const int j = st * TK + lane;
+    if (lane < TK) {
+      if constexpr (FP8) s *= ue8m0_to_f32(kscale[wave][min(j, kDecPerWave - 1)]);
+      sc[wave][j] = s;
     }
   }
+  // one coalesced store of this wave's scores
+  __builtin_amdgcn_s_waitcnt(0xc07f);            // lgkmcnt(0): own LDS writes done
+  for (int j = lane; j < nk; j += 64) out[w0 + j] = sc[wave][j];
 }
 
 // ----------------------------------------------------- prefill shape -------
@@ -311,9 +365,8 @@ int pick_ksplit(int blocks, int ntiles_max) {
 template <bool FP8>
 hipError_t launch_mfma(const IndexLaunch& a, hipStream_t s) {
   if (a.q_count <= 4) {
-    const int chunk = 2048;
-    dim3 grid((a.Lk + chunk - 1) / chunk, a.B * a.q_count);
-    hipLaunchKernelGGL(idx_decode_kernel<FP8>, grid, dim3(256), 0, s, a, chunk);
+    dim3 grid((a.Lk + kDecChunk - 1) / kDecChunk, a.B * a.q_count);
+    hipLaunchKernelGGL(idx_decode_kernel<FP8>, grid, dim3(256), 0, s, a);
   } else {
     constexpr int QB = 8;
     const int nqb = (a.q_count + QB - 1) / QB;

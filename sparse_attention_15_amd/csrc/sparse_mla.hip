@@ -61,13 +61,6 @@ typedef short i16x4 __attribute__((ext_vector_type(4)));
 // keep every operand address a per-lane base plus a compile-time offset.
 __device__ __forceinline__ int swz(int r) { return ((r >> 2) + 1) & 3; }
 
-// s_waitcnt on the vector-memory counter only (gfx9 encoding: expcnt and
-// lgkmcnt fields left at their maxima).
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | (((N >> 4) & 3) << 14));
-}
-
 // 16-byte global -> LDS copy per lane (LDS destination = lds_base + 16*lane,
 // global source = gbase + row_off + (map >> 8)).  Written as asm so that the
 // compiler's wait-count pass does not treat the in-flight copies into other
@@ -93,10 +86,6 @@ __device__ __forceinline__ void dma16(const void* gbase, uint32_t row_off, uint3
       : "m0");
 }
 #pragma clang diagnostic pop
-
-__device__ __forceinline__ uint32_t lds_addr(const void* p) {
-  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) uint8_t*)(p);
-}
 
 // max over lanes l and l ^ 32 (v_permlane32_swap exchanges the two halves
 // of the wave without going through LDS)
