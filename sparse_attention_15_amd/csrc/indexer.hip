@@ -202,14 +202,6 @@ __global__ __launch_bounds__(256, 2) void idx_decode_kernel(IndexLaunch a) {
 
   const int64_t qrow = (int64_t)b * a.Lq + i;
   const uint8_t* kbase = static_cast<const uint8_t*>(a.k) + (int64_t)b * a.Lk * ROWB;   // wave-uniform
-  if constexpr (FP8) {
-    const uint8_t* ks = a.k_scale + (int64_t)b * a.Lk;
-    for (int j = lane; j < nk; j += 64) kscale[wave][j] = ks[w0 + j];
-  }
-  QFrag<FP8> q;
-  float wv[16];
-  load_query<FP8>(a, qrow, lane, q, wv);
-  wait_vmcnt<0>();                               // from here on only the copies use the counter
 
   // copy k of a stage fills LDS slots 64k + lane: row slot/CPR, stored
   // position slot%CPR, holding global chunk position ^ (row % CPR)
@@ -230,9 +222,31 @@ __global__ __launch_bounds__(256, 2) void idx_decode_kernel(IndexLaunch a) {
       lds_dma16(kbase, (uint32_t)key * ROWB + dchk[k] * 16, dst + 1024 * k);
     }
   };
+  // first stages in flight before the query loads, so both latencies overlap
 #pragma unroll
   for (int st = 0; st < kDecRing - 1; ++st)
     if (st < nst) issue(st);
+  if constexpr (FP8) {
+    const uint8_t* ks = a.k_scale + (int64_t)b * a.Lk;
+    for (int j = lane; j < nk; j += 64) kscale[wave][j] = ks[w0 + j];
+  }
+  QFrag<FP8> q;
+  float wv[16];
+  load_query<FP8>(a, qrow, lane, q, wv);
+  // Wait for everything issued so far (the query loads are the youngest), so
+  // that inside the loop only the copies use the vector-memory counter.
+  wait_vmcnt<0>();
+  if constexpr (!FP8) {
+#pragma unroll
+    for (int m = 0; m < 4; ++m)
+#pragma unroll
+      for (int t = 0; t < 4; ++t) asm volatile("" : "+v"(q.v[m][t]));
+  } else {
+#pragma unroll
+    for (int m = 0; m < 4; ++m) asm volatile("" : "+v"(q.v[m]));
+  }
+#pragma unroll
+  for (int e = 0; e < 16; ++e) asm volatile("" : "+v"(wv[e]));
 
   const int r16 = lane & 15, g = lane >> 4;
   for (int st = 0; st < nst; ++st) {

@@ -13,7 +13,8 @@
 // The selection is then {key > T} plus the first r positions with key == T,
 // and one ordered pass writes it: for a chosen element at position x its
 // output slot is  #(key > T before x) + min(#(key == T before x), r),
-// so a single block-wide scan of packed (gt, eq) counts gives the slots.
+// so block-wide scans of packed (gt, eq) counts give the slots (DPP wave
+// scans, one barrier per group of 8 chunks).
 // Row values stay in registers (4 consecutive positions per 16-byte load);
 // rows longer than the register budget are re-read from memory each pass.
 #include "dsa_device.h"
@@ -31,19 +32,31 @@ __device__ __forceinline__ uint32_t order_key(float x) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-// Inclusive scan over the wave.
-__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t v, int lane) {
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const uint32_t y = __shfl_up(v, off, 64);
-    if (lane >= off) v += y;
-  }
+// DPP source shift (lanes whose source is out of range read 0).
+template <int CTRL, int ROWS>
+__device__ __forceinline__ uint32_t dpp(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, ROWS, 0xf, false);
+}
+
+// Inclusive scan over the 64 lanes: shifts by 1, 2, 4, 8 within each row of
+// 16 lanes, then row 0's total into row 1 and row 2's into row 3
+// (row_bcast:15), then lane 31's running total into rows 2 and 3
+// (row_bcast:31).
+__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t v, int) {
+  v += dpp<0x111, 0xf>(v);
+  v += dpp<0x112, 0xf>(v);
+  v += dpp<0x114, 0xf>(v);
+  v += dpp<0x118, 0xf>(v);
+  v += dpp<0x142, 0xa>(v);
+  v += dpp<0x143, 0xc>(v);
   return v;
 }
 
+constexpr int kGroup = 8;            // chunks per emission group
+
 struct Shared {
   uint32_t hist[4096];
-  uint32_t wsum[kWaves];
+  uint32_t wsum[kGroup * kWaves];
   uint32_t bin;        // chosen bin of the current pass
   uint32_t above;      // elements in bins above it
 };
@@ -159,49 +172,70 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(TopkLaunch a) {
   }
 
   // Ordered emission: chunk c holds positions 4*(c*kThreads + tid) + 0..3,
-  // so scanning threads in order scans positions in order.
+  // so positions run over (chunk, thread, element).  A group of chunks is
+  // scanned at once (one barrier): per chunk a block-wide exclusive scan of
+  // the packed (gt, eq) counts, plus running totals over earlier chunks.
   uint32_t gt_run = 0, eq_run = 0;                // counts over earlier chunks
-  auto emit = [&](int c, const uint32_t (&kk)[4]) {
-    uint32_t gt[4], eq[4], packed = 0;
+  constexpr int GS = NC >= 16 ? kGroup / 2 : kGroup;   // register budget of the widest variant
+  auto emit_group = [&](int c0, int G, const uint32_t (*kk)[4]) {
+    uint32_t packed[GS], incl[GS];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const uint32_t m = kk[e] & mask;
-      gt[e] = (kk[e] != 0u && m > prefix) ? 1u : 0u;
-      eq[e] = (kk[e] != 0u && m == prefix) ? 1u : 0u;
-      packed += gt[e] | (eq[e] << 16);
+    for (int g = 0; g < GS; ++g) {
+      if (g < G) {
+        uint32_t pk = 0;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const uint32_t m = kk[g][e] & mask;
+          const bool valid = kk[g][e] != 0u;
+          pk += (valid && m > prefix) ? 1u : 0u;
+          pk += (valid && m == prefix) ? 0x10000u : 0u;
+        }
+        packed[g] = pk;
+        incl[g] = wave_incl_scan(pk, lane);
+        if (lane == 63) sh.wsum[g * kWaves + wave] = incl[g];
+      }
     }
-    const uint32_t incl = wave_incl_scan(packed, lane);
-    if (lane == 63) sh.wsum[wave] = incl;
     __syncthreads();
-    uint32_t before = 0, total = 0;
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w) {
-      const uint32_t v = sh.wsum[w];
-      before += (w < wave) ? v : 0u;
-      total += v;
-    }
-    const uint32_t excl = before + incl - packed;
-    uint32_t g_b = gt_run + (excl & 0xffffu), e_b = eq_run + (excl >> 16);
-    const int pos0 = (c * kThreads + tid) * 4;
+    for (int g = 0; g < GS; ++g) {
+      if (g < G) {
+        uint32_t before = 0, total = 0;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      if (gt[e] || (eq[e] && e_b < k_rem)) out[g_b + min(e_b, k_rem)] = pos0 + e;
-      g_b += gt[e];
-      e_b += eq[e];
+        for (int w = 0; w < kWaves; ++w) {
+          const uint32_t v = sh.wsum[g * kWaves + w];
+          before += (w < wave) ? v : 0u;
+          total += v;
+        }
+        const uint32_t excl = before + incl[g] - packed[g];
+        uint32_t g_b = gt_run + (excl & 0xffffu), e_b = eq_run + (excl >> 16);
+        const int pos0 = ((c0 + g) * kThreads + tid) * 4;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const uint32_t m = kk[g][e] & mask;
+          const bool valid = kk[g][e] != 0u;
+          const bool gt = valid && m > prefix, eq = valid && m == prefix;
+          if (gt || (eq && e_b < k_rem)) out[g_b + min(e_b, k_rem)] = pos0 + e;
+          g_b += gt ? 1u : 0u;
+          e_b += eq ? 1u : 0u;
+        }
+        gt_run += total & 0xffffu;
+        eq_run += total >> 16;
+      }
     }
-    gt_run += total & 0xffffu;
-    eq_run += total >> 16;
-    __syncthreads();
+    __syncthreads();                              // wsum is reused by the next group
   };
   if constexpr (NC > 0) {
 #pragma unroll
-    for (int c = 0; c < NC; ++c)
-      if (c < iters) emit(c, keys[c]);
+    for (int c0 = 0; c0 < NC; c0 += GS)
+      if (c0 < iters) emit_group(c0, min(GS, iters - c0), keys + c0);
   } else {
-    for (int c = 0; c < iters; ++c) {
-      uint32_t kk[4];
-      load_keys(c, kk);
-      emit(c, kk);
+    for (int c0 = 0; c0 < iters; c0 += GS) {
+      uint32_t kk[GS][4];
+      const int G = min(GS, iters - c0);
+#pragma unroll
+      for (int g = 0; g < GS; ++g)
+        if (g < G) load_keys(c0 + g, kk[g]);
+      emit_group(c0, G, kk);
     }
   }
   // K' = min(K, n) = K here (n > K), so no padding is needed.
