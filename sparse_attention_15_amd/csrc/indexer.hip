@@ -280,20 +280,24 @@ __global__ __launch_bounds__(256, 2) void idx_decode_kernel(IndexLaunch a) {
 // ----------------------------------------------------- prefill shape -------
 // grid (ceil(q_count / QB), ksplit, B), QB waves = QB consecutive queries.
 // The block walks 64-key tiles kt = blockIdx.y, +ksplit, ... up to the last
-// query's causal limit; each tile is staged once in LDS (16-byte chunks
-// XOR-swizzled by row so the MFMA operand reads are bank-conflict free) and
-// consumed by all QB waves.
+// query's causal limit.  Tiles stream through a 4-deep LDS ring filled by
+// LDS-DMA (whole key rows per copy instruction, chunks XOR-permuted by row so
+// the MFMA operand reads are conflict-free); each tile is consumed by all QB
+// waves, with one barrier per tile.
+constexpr int kPreRing = 4;
+
 template <bool FP8, int QB>
 __global__ __launch_bounds__(QB * 64) void idx_prefill_kernel(IndexLaunch a, int ksplit) {
   constexpr int TK = 64;
   constexpr int ROWB = FP8 ? kD : 2 * kD;        // bytes per key row
   constexpr int CPR = ROWB / 16;                  // 16-byte chunks per row
-  constexpr int NT = QB * 64;
-  constexpr int CPT = TK * CPR / NT;              // chunks per thread per tile
-  static_assert(CPT >= 1 && TK * CPR % NT == 0, "tile/threads mismatch");
-  __shared__ __attribute__((aligned(16))) uint8_t lds[2][TK * ROWB];
+  constexpr int STG = TK * ROWB;                  // bytes per tile
+  constexpr int NDMA = STG / 1024;                // copy instructions per tile
+  static_assert(NDMA % QB == 0 || QB % NDMA == 0, "tile copies must split evenly over the waves");
+  constexpr int DPW = NDMA >= QB ? NDMA / QB : 1; // copies per wave (waves >= NDMA issue none)
+  __shared__ __attribute__((aligned(16))) uint8_t ring[kPreRing][STG];
 
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int qb = gridDim.x - 1 - blockIdx.x;      // longest rows first
   const int b = blockIdx.z;
   const int ii = qb * QB + wave;
@@ -305,48 +309,62 @@ __global__ __launch_bounds__(QB * 64) void idx_prefill_kernel(IndexLaunch a, int
   const int ntiles = (n_max + TK - 1) / TK;
   const int row = b * a.q_count + ii;
   float* out = a.scores + (int64_t)row * a.row_stride;
+  const uint8_t* kbase = static_cast<const uint8_t*>(a.k) + (int64_t)b * a.Lk * ROWB;   // uniform
+  const uint8_t* ks = FP8 ? a.k_scale + (int64_t)b * a.Lk : nullptr;
+
+  // this block's tiles: kt = blockIdx.y + ksplit * j, j < nj
+  const int nj = blockIdx.y < ntiles ? (ntiles - 1 - blockIdx.y) / ksplit + 1 : 0;
+  // copy c (wave's k-th, c = wave * DPW + k) fills LDS slots 64c + lane: row
+  // slot/CPR, stored position slot%CPR, holding global chunk position ^ row
+  int drow[DPW], dchk[DPW];
+#pragma unroll
+  for (int k = 0; k < DPW; ++k) {
+    const int slot = 64 * (wave * DPW + k) + lane;
+    drow[k] = slot / CPR;
+    dchk[k] = (slot % CPR) ^ (drow[k] & (CPR - 1));
+  }
+  const bool copies = wave * DPW < NDMA;
+  const uint32_t ring_lds = lds_addr(&ring[0][0]);
+  auto issue = [&](int j) {
+    if (!copies) return;
+    const int k0 = (blockIdx.y + ksplit * j) * TK;
+    const uint32_t dst = __builtin_amdgcn_readfirstlane(ring_lds + (j % kPreRing) * STG);
+#pragma unroll
+    for (int k = 0; k < DPW; ++k) {
+      const int key = min(k0 + drow[k], a.Lk - 1);   // rows past the end repeat the last key
+      lds_dma16(kbase, (uint32_t)key * ROWB + dchk[k] * 16, dst + 1024 * (wave * DPW + k));
+    }
+  };
+#pragma unroll
+  for (int j = 0; j < kPreRing - 1; ++j)
+    if (j < nj) issue(j);
 
   QFrag<FP8> q;
   float wv[16];
   if (active) load_query<FP8>(a, (int64_t)b * a.Lq + i, lane, q, wv);
-  const uint8_t* kbase = static_cast<const uint8_t*>(a.k) + (int64_t)b * a.Lk * ROWB;
-  const uint8_t* ks = FP8 ? a.k_scale + (int64_t)b * a.Lk : nullptr;
-
-  u32x4 stage[CPT];
-  auto gload = [&](int kt) {
-#pragma unroll
-    for (int c = 0; c < CPT; ++c) {
-      const int cid = threadIdx.x + c * NT;
-      const int r = cid / CPR, ch = cid % CPR;
-      const int key = min(kt * TK + r, a.Lk - 1);
-      stage[c] = ld16(kbase + (int64_t)key * ROWB + ch * 16);
-    }
-  };
-  auto lstore = [&](int buf) {
-#pragma unroll
-    for (int c = 0; c < CPT; ++c) {
-      const int cid = threadIdx.x + c * NT;
-      const int r = cid / CPR, ch = cid % CPR;
-      st16(&lds[buf][r * ROWB + ((ch ^ (r & (CPR - 1))) * 16)], stage[c]);
-    }
-  };
+  wait_vmcnt<0>();                                // prologue loads complete; only copies and
+                                                  // score stores use the counter from here on
 
   const int r16 = lane & 15, g = lane >> 4;
-  int kt = blockIdx.y;
-  int buf = 0;
-  if (kt < ntiles) {
-    gload(kt);
-    lstore(0);
-  }
-  __syncthreads();
-  for (; kt < ntiles; kt += ksplit) {
-    const int nk = kt + ksplit;
-    if (nk < ntiles) gload(nk);
+  for (int j = 0; j < nj; ++j) {
+    // tile j is complete once at most this wave's copies of the later tiles
+    // remain (score stores, which may also be outstanding, only make the
+    // wait stricter)
+    if (copies) {
+      if (j + 2 < nj) wait_vmcnt<2 * DPW>();
+      else if (j + 1 < nj) wait_vmcnt<DPW>();
+      else wait_vmcnt<0>();
+    }
+    __builtin_amdgcn_s_barrier();                 // every wave's copies of tile j landed, tile j-1 is free
+    asm volatile("" ::: "memory");
+    if (j + kPreRing - 1 < nj) issue(j + kPreRing - 1);
+    const int kt = blockIdx.y + ksplit * j;
     if (active && kt * TK <= p) {
+      const uint8_t* tile = &ring[j % kPreRing][0];
 #pragma unroll
-      for (int j = 0; j < TK / 16; ++j) {
-        const int rr = 16 * j + r16;
-        const uint8_t* lrow = &lds[buf][rr * ROWB];
+      for (int st = 0; st < TK / 16; ++st) {
+        const int rr = 16 * st + r16;
+        const uint8_t* lrow = tile + rr * ROWB;
         KFrag<FP8> kf;
         if constexpr (!FP8) {
 #pragma unroll
@@ -355,16 +373,13 @@ __global__ __launch_bounds__(QB * 64) void idx_prefill_kernel(IndexLaunch a, int
           kf.v = join(ld16(lrow + (((2 * g) ^ (rr & 7)) * 16)), ld16(lrow + (((2 * g + 1) ^ (rr & 7)) * 16)));
         }
         float s = tile_score<FP8>(q, kf, wv);
-        const int key = kt * TK + 16 * j + lane;
+        const int key = kt * TK + 16 * st + lane;
         if (lane < 16 && key <= p) {
           if constexpr (FP8) s *= ue8m0_to_f32(ks[key]);
           out[key] = s;
         }
       }
     }
-    if (nk < ntiles) lstore(buf ^ 1);
-    __syncthreads();
-    buf ^= 1;
   }
   if (a.write_masked && active && blockIdx.y == 0)
     for (int s = p + 1 + lane; s < a.Lk; s += 64) out[s] = kNegInf;
