@@ -67,6 +67,18 @@ __device__ __forceinline__ float wave_sum(float v) {
   return v;
 }
 
+// Values of lanes l and l ^ 32 (v_permlane32_swap exchanges lanes 32..63 of
+// its first operand with lanes 0..31 of its second; with both holding x,
+// they end up as x[l] and x[l ^ 32] in some order).  Written as asm with two
+// distinct in/out registers; the VALU writes of the copies need two wait
+// states before the permute reads them.
+__device__ __forceinline__ void xor32_pair(float x, float& a, float& b) {
+  uint32_t u = __builtin_bit_cast(uint32_t, x), v = u;
+  asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1" : "+v"(u), "+v"(v));
+  a = __builtin_bit_cast(float, u);
+  b = __builtin_bit_cast(float, v);
+}
+
 // s_waitcnt on the vector-memory counter only (gfx9 encoding: expcnt and
 // lgkmcnt fields left at their maxima).
 template <int N>

@@ -153,9 +153,12 @@ __device__ __forceinline__ float tile_score(const QFrag<FP8>& q, const KFrag<FP8
   for (int m = 0; m < 4; ++m)
 #pragma unroll
     for (int j = 0; j < 4; ++j) s = fmaf(wv[4 * m + j], fmaxf(acc[m][j], 0.f), s);
+  // sum over the four 16-lane groups: a shuffle across 16 lanes, then the
+  // two halves of the wave through v_permlane32_swap
   s += shfl_xor(s, 16);
-  s += shfl_xor(s, 32);
-  return s;
+  float lo, hi;
+  xor32_pair(s, lo, hi);
+  return lo + hi;
 }
 
 // ------------------------------------------------------ decode shape -------

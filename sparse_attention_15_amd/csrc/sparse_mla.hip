@@ -87,12 +87,11 @@ __device__ __forceinline__ void dma16(const void* gbase, uint32_t row_off, uint3
 }
 #pragma clang diagnostic pop
 
-// max over lanes l and l ^ 32 (v_permlane32_swap exchanges the two halves
-// of the wave without going through LDS)
+// max over lanes l and l ^ 32 (v_permlane32_swap, no LDS round trip)
 __device__ __forceinline__ float max_xor32(float x) {
-  const auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, x), __builtin_bit_cast(uint32_t, x),
-                                                  false, false);
-  return fmaxf(__builtin_bit_cast(float, r[0]), __builtin_bit_cast(float, r[1]));
+  float a, b;
+  xor32_pair(x, a, b);
+  return fmaxf(a, b);
 }
 
 __device__ __forceinline__ u32x2 tr_read(const uint8_t* p) {
