@@ -206,10 +206,16 @@ __device__ __forceinline__ void attn_block(AttnState& st, const uint8_t* buf, ui
         dma16(g.kvb, roff[k], dma_map[k], __builtin_amdgcn_readfirstlane(g.dst + (g.dfirst + k) * 1024));
     }
   }
-  // scaled base-2 logits; keys not listed in this block (bit clear in
-  // vmask) get -inf.  This lane's keys: 8q + 4hf + r.
+  // base-2 logits z = zscale * s.  With zscale > 0 (the usual case) the scale
+  // is folded into the exponent's FMA and the max is taken on raw scores;
+  // otherwise the scores are scaled first.  Keys not listed in this block
+  // (bit clear in vmask) get -inf.  This lane's keys: 8q + 4hf + r.
+  float fs = zscale;
+  if (!(zscale > 0.f)) {
 #pragma unroll
-  for (int e = 0; e < 16; ++e) s[e] *= zscale;
+    for (int e = 0; e < 16; ++e) s[e] *= zscale;
+    fs = 1.f;
+  }
   if (vmask != 0xffffffffu) {
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
@@ -221,7 +227,7 @@ __device__ __forceinline__ void attn_block(AttnState& st, const uint8_t* buf, ui
 #pragma unroll
   for (int e = 3; e < 15; e += 2) mb = fmaxf(fmaxf(mb, s[e]), s[e + 1]);
   mb = fmaxf(mb, s[15]);
-  mb = max_xor32(mb);
+  mb = max_xor32(mb) * fs;
   if (__ballot(mb > st.m_run + kTau)) {
     const float m_new = fmaxf(st.m_run, mb);
     if (__ballot(st.m_run != kNegInf)) {          // before the first raise O and l are zero
@@ -232,32 +238,32 @@ __device__ __forceinline__ void attn_block(AttnState& st, const uint8_t* buf, ui
     }
     st.m_run = m_new;
   }
-  const float mref = (st.m_run == kNegInf) ? 0.f : st.m_run;
+  const float nref = (st.m_run == kNegInf) ? 0.f : -st.m_run;
   // p = 2^(z - m) <= 2^kTau; P is rounded to bf16 for the MFMA, the
   // normaliser sums the fp32 values (the rounding is unbiased and far below
-  // the output rounding)
-  u32x4 pb[2];
+  // the output rounding).  The two 16-key halves of P feed the two PV k-steps,
+  // so the second half's exponentials can overlap the first half's MFMAs.
   float lsum = 0.f;
-#pragma unroll
-  for (int k = 0; k < 2; ++k)
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const float p0 = __builtin_amdgcn_exp2f(s[8 * k + 2 * e] - mref);
-      const float p1 = __builtin_amdgcn_exp2f(s[8 * k + 2 * e + 1] - mref);
-      pb[k][e] = pack_bf16x2(p0, p1);
-      lsum += p0 + p1;
-    }
-  st.l_run += lsum;
   // O^T[v][head] += V^T[v][key] . P^T[key][head]
 #pragma unroll
-  for (int vt = 0; vt < kVTiles; ++vt)
+  for (int k = 0; k < 2; ++k) {
+    u32x4 pb;
 #pragma unroll
-    for (int k = 0; k < 2; ++k) {
+    for (int e = 0; e < 4; ++e) {
+      const float p0 = __builtin_amdgcn_exp2f(fmaf(s[8 * k + 2 * e], fs, nref));
+      const float p1 = __builtin_amdgcn_exp2f(fmaf(s[8 * k + 2 * e + 1], fs, nref));
+      pb[e] = pack_bf16x2(p0, p1);
+      lsum += p0 + p1;
+    }
+#pragma unroll
+    for (int vt = 0; vt < kVTiles; ++vt) {
       const u32x2 lo = tr_read(buf + pv_off[k][0] + 64 * vt);
       const u32x2 hi = tr_read(buf + pv_off[k][1] + 64 * vt);
       const u32x4 av = {lo[0], lo[1], hi[0], hi[1]};
-      st.o[vt] = mfma32(av, pb[k], st.o[vt]);
+      st.o[vt] = mfma32(av, pb, st.o[vt]);
     }
+  }
+  st.l_run += lsum;
 }
 
 __global__ __launch_bounds__(kWavesA * 64, 1) void attn_bf16_kernel(AttnLaunch a) {
@@ -422,54 +428,60 @@ __global__ __launch_bounds__(kWavesA * 64, 1) void attn_bf16_kernel(AttnLaunch a
   const float l_tot = st.l_run + shfl_xor(st.l_run, 32);
   const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
   const float lse = l_tot > 0.f ? (st.m_run + log2f(l_tot)) * kLn2 : kNegInf;
-  const int vbase = 4 * hf;
+
+  // Output rows (out, or this split's partials) through LDS: per pass the
+  // wave writes a slice of its 32 head rows (512 bytes each) into the now
+  // idle stage buffers, then stores 1 KB contiguous per instruction (two
+  // 512-byte row segments) instead of 16 bytes into each of 32 rows.
+  __syncthreads();                                // every wave is done with the stage buffers
+  const bool f32 = a.out_f32 != 0;
+  uint8_t* dst_base;
   if (a.splits == 1) {
-    if (a.out_f32) {
-      float* op = static_cast<float*>(a.out) + (qrow * kNH + h) * kDv + vbase;
-#pragma unroll
-      for (int vt = 0; vt < kVTiles; ++vt)
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const f32x4 v4 = {st.o[vt][4 * q] * inv, st.o[vt][4 * q + 1] * inv, st.o[vt][4 * q + 2] * inv,
-                            st.o[vt][4 * q + 3] * inv};
-          *reinterpret_cast<f32x4*>(op + 32 * vt + 8 * q) = v4;
-        }
-    } else {
-      uint16_t* op = static_cast<uint16_t*>(a.out) + (qrow * kNH + h) * kDv + vbase;
-#pragma unroll
-      for (int vt = 0; vt < kVTiles; ++vt)
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const u32x2 v2 = {pack_bf16x2(st.o[vt][4 * q] * inv, st.o[vt][4 * q + 1] * inv),
-                            pack_bf16x2(st.o[vt][4 * q + 2] * inv, st.o[vt][4 * q + 3] * inv)};
-          *reinterpret_cast<u32x2*>(op + 32 * vt + 8 * q) = v2;
-        }
-    }
+    dst_base = static_cast<uint8_t*>(a.out) + (qrow * kNH + 32 * wave) * (int64_t)kDv * (f32 ? 4 : 2);
     if (a.lse && hf == 0) a.lse[qrow * kNH + h] = lse;
   } else {
     const int64_t prow = (int64_t)rr * a.splits + split;
-    if (a.out_f32) {
-      float* op = static_cast<float*>(a.part_o) + (prow * kNH + h) * kDv + vbase;
+    dst_base = static_cast<uint8_t*>(a.part_o) + (prow * kNH + 32 * wave) * (int64_t)kDv * (f32 ? 4 : 2);
+    if (hf == 0) a.part_lse[prow * kNH + h] = lse;
+  }
+  constexpr int kEpiRow = 528;                    // 512 bytes + 16 bytes of padding per head row
+  uint8_t* ebuf = stg + wave * 32 * kEpiRow;
+  const int row_bytes = kDv * (f32 ? 4 : 2);
+  auto flush = [&](int pass) {                    // ebuf rows -> bytes [512 pass, +512) of each head row
+    __builtin_amdgcn_s_waitcnt(0xc07f);           // lgkmcnt(0): this wave's LDS writes are done
 #pragma unroll
-      for (int vt = 0; vt < kVTiles; ++vt)
+    for (int it = 0; it < 16; ++it) {
+      const int r = 2 * it + (lane >> 5);
+      const u32x4 v = ld16(ebuf + r * kEpiRow + 16 * (lane & 31));
+      st16(dst_base + (int64_t)r * row_bytes + 512 * pass + 16 * (lane & 31), v);
+    }
+  };
+  if (f32) {
+#pragma unroll
+    for (int pass = 0; pass < 4; ++pass) {        // 4 value tiles (128 dims) per pass
+#pragma unroll
+      for (int vt = 4 * pass; vt < 4 * pass + 4; ++vt)
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           const f32x4 v4 = {st.o[vt][4 * q] * inv, st.o[vt][4 * q + 1] * inv, st.o[vt][4 * q + 2] * inv,
                             st.o[vt][4 * q + 3] * inv};
-          *reinterpret_cast<f32x4*>(op + 32 * vt + 8 * q) = v4;
+          *reinterpret_cast<f32x4*>(ebuf + c32 * kEpiRow + ((vt - 4 * pass) * 32 + 8 * q + 4 * hf) * 4) = v4;
         }
-    } else {
-      uint16_t* op = static_cast<uint16_t*>(a.part_o) + (prow * kNH + h) * kDv + vbase;
+      flush(pass);
+    }
+  } else {
 #pragma unroll
-      for (int vt = 0; vt < kVTiles; ++vt)
+    for (int pass = 0; pass < 2; ++pass) {        // 8 value tiles (256 dims) per pass
+#pragma unroll
+      for (int vt = 8 * pass; vt < 8 * pass + 8; ++vt)
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           const u32x2 v2 = {pack_bf16x2(st.o[vt][4 * q] * inv, st.o[vt][4 * q + 1] * inv),
                             pack_bf16x2(st.o[vt][4 * q + 2] * inv, st.o[vt][4 * q + 3] * inv)};
-          *reinterpret_cast<u32x2*>(op + 32 * vt + 8 * q) = v2;
+          *reinterpret_cast<u32x2*>(ebuf + c32 * kEpiRow + ((vt - 8 * pass) * 32 + 8 * q + 4 * hf) * 2) = v2;
         }
+      flush(pass);
     }
-    if (hf == 0) a.part_lse[prow * kNH + h] = lse;
   }
 }
 
