@@ -196,6 +196,9 @@ def main():
     ap.add_argument("--sets", type=int, default=3, help="rotating input sets")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--out-dtype", default=None)
+    ap.add_argument("--with-producer", action="store_true",
+                    help="FP8-index workloads: start each step from bf16 index activations and run the FP8 "
+                         "producer (Hadamard rotation + ue8m0/E4M3 quantisation) before the fused path")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a 1 GiB elementwise copy (for calibrating rocprofv3 byte counters)")
     args = ap.parse_args()
@@ -216,7 +219,23 @@ def main():
     torch.cuda.set_device(0)
     p = dsa.make_problem(cfg, out_dtype=args.out_dtype)
     nsets = max(1, args.sets if cfg.q_len <= 4 else min(args.sets, 2))
-    sets = [generate(cfg, device=dev, set_index=s) for s in range(nsets)]
+    producer = args.with_producer
+    if producer and cfg.index_dtype != "fp8_e4m3":
+        print("--with-producer applies to FP8-index workloads only", file=sys.stderr)
+        sys.exit(2)
+    if producer:
+        # bf16 index activations of the same shapes; the FP8 inputs are
+        # produced inside every step
+        from dsa_workloads import scaled
+        cfg16 = scaled(cfg, index_dtype="bf16")
+        sets = [generate(cfg16, device=dev, set_index=s) for s in range(nsets)]
+        for st_ in sets:
+            st_["q_codes"] = torch.empty(st_["q_idx"].shape, dtype=torch.uint8, device=dev)
+            st_["q_scale"] = torch.empty(st_["q_idx"].shape[:-1], dtype=torch.uint8, device=dev)
+            st_["k_codes"] = torch.empty(st_["k_idx"].shape, dtype=torch.uint8, device=dev)
+            st_["k_scale"] = torch.empty(st_["k_idx"].shape[:-1], dtype=torch.uint8, device=dev)
+    else:
+        sets = [generate(cfg, device=dev, set_index=s) for s in range(nsets)]
     ws = torch.empty(dsa.workspace_size(p, dsa.DSA_OP_FORWARD), dtype=torch.uint8, device=dev)
     odt = torch.float32 if p.out_dtype == dsa.DSA_F32 else torch.bfloat16
     outs = [torch.empty(cfg.batch, cfg.q_len, cfg.attn_heads, cfg.v_dim, dtype=odt, device=dev) for _ in sets]
@@ -224,14 +243,27 @@ def main():
     n_chunks = dsa.forward_chunks(p)
     slots_per_step = n_chunks * dsa.DSA_NUM_STAGES
 
+    prod_ev = []
+
     def step(k, events=None, base=0):
         s = sets[k % nsets]
+        q_idx, k_idx = s["q_idx"], s["k_idx"]
+        if producer:
+            if events is not None:
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record()
+            dsa.index_rotate_quantize(s["q_idx"], s["q_codes"], s["q_scale"])
+            dsa.index_rotate_quantize(s["k_idx"], s["k_codes"], s["k_scale"])
+            if events is not None:
+                e1.record()
+                prod_ev.append((e0, e1))
+            q_idx, k_idx = s["q_codes"], s["k_codes"]
         ev = None
         if events is not None:
             import ctypes
             ev = ctypes.cast(ctypes.byref(events.arr, ctypes.sizeof(ctypes.c_void_p) * 2 * base),
                              ctypes.POINTER(ctypes.c_void_p))
-        dsa.forward(p, s["q_idx"], s["q_scale"], s["k_idx"], s["k_scale"], s["head_w"], s["q_attn"], s["kv"],
+        dsa.forward(p, q_idx, s["q_scale"], k_idx, s["k_scale"], s["head_w"], s["q_attn"], s["kv"],
                     out=outs[k % nsets], lse=lses[k % nsets], workspace=ws, events=ev,
                     n_events=2 * slots_per_step)
 
@@ -280,6 +312,16 @@ def main():
                 traffic=measured_traffic(kname, cfg.name), kernel=kname,
                 launch_us=round(launch_ms * 1e3, 2), per_launch=f"{units:.0f} {desc}")
     path_bytes = al["index_bytes"] + al["attn_bytes"]
+    prod = None
+    if producer:
+        prod_ms = sum(a.elapsed_time(b) for a, b in prod_ev) / max(1, len(prod_ev))
+        prows = cfg.batch * cfg.q_len * cfg.index_heads + cfg.batch * cfg.kv_len
+        pbytes = prows * (cfg.index_dim * 2 + cfg.index_dim + 1)      # bf16 in, codes + scale byte out
+        gbs = pbytes / (prod_ms * 1e-3) / 1e9
+        prod = dict(kernel="rotate_quant_kernel", rows_per_step=prows, ms_per_step=round(prod_ms, 5),
+                    algorithmic_bytes=pbytes, achieved=round(gbs, 1), unit="GB/s", peak=HBM_PEAK_GBS,
+                    frac=round(gbs / HBM_PEAK_GBS, 4),
+                    note="q rows (B*Lq*H) and key rows (B*Lk): 128 bf16 in, 128 E4M3 codes + 1 scale byte out")
     res = {
         "metric": "DSA queries/sec (indexer+top-k+sparse MLA)",
         "value": round(qps, 1),
@@ -293,13 +335,14 @@ def main():
         "vs_baseline": None,
         "dtype": {"bf16": "bf16", "f32": "f32", "fp8_e4m3": "fp8_e4m3+bf16"}[cfg.index_dtype],
         "data": "synthetic (seeded generators; no dataset or weights)",
-        "config": {"workload": cfg.name, "batch": cfg.batch, "q_len": cfg.q_len, "kv_len": cfg.kv_len,
+        "config": {"workload": cfg.name + ("+fp8_producer" if producer else ""), "batch": cfg.batch, "q_len": cfg.q_len, "kv_len": cfg.kv_len,
                    "index_heads": cfg.index_heads, "index_dim": cfg.index_dim, "topk": cfg.topk,
                    "attn_heads": cfg.attn_heads, "qk_dim": cfg.qk_dim, "v_dim": cfg.v_dim,
                    "query_chunks": n_chunks, "attn_splits": splits, "input_sets": nsets},
         "roofline": roof,
         "stage_ms": {name: round(v, 5) for name, v in zip(dsa.STAGE_NAMES, stage_ms)},
         "ms_per_step_evented": round(evented_ms, 5),
+        **({"producer": prod} if prod else {}),
         "path_hbm_frac": round(path_bytes / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
         "path_algorithmic_bytes": path_bytes,
         "path_mfma_frac_bf16": round((al["index_flops"] + al["attn_flops"]) / (ms_per_step * 1e-3) / 1e12

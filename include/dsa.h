@@ -175,6 +175,27 @@ dsa_status_t dsa_forward_timed(const dsa_problem_t* prob,
                                int32_t* n_chunks_out,
                                hipStream_t stream);
 
+/* FP8 producer of the index vectors (HF doc "DeepSeek-V3.2", section
+ * "DeepSeek Sparse Attention (DSA)", item 1: the indexer runs in FP8 after an
+ * orthogonal Hadamard rotation; "scale_fmt: ue8m0" in the released
+ * configuration excerpt of the atlas "DeepSeek-V3.2-Exp" token-ids page).
+ * Produces dsa_index_scores' FP8 inputs from bf16 / f32 activations: call it
+ * once for the query rows ([B][Lq][H] rows) and once for the key rows
+ * ([B][Lk] rows).
+ *   x       [rows][dim] x_dtype (DSA_BF16 or DSA_F32), device
+ *   codes   [rows][dim] uint8 out, device: E4M3 codes of y / 2^e
+ *   scales  [rows] uint8 out, device: e + 127
+ *   y = H x / sqrt(dim), H the Sylvester Hadamard matrix (H_1 = [1],
+ *   H_2m = [[H_m, H_m], [H_m, -H_m]]), computed in fp32 as butterflies over
+ *   strides 1, 2, ..., dim/2 followed by one multiply by fp32(1/sqrt(dim));
+ *   e is the smallest integer with max|y| / 2^e <= 448 (0 for an all-zero
+ *   row, clamped at -127); codes round to nearest, ties to even.
+ *   dim must be 128 (else DSA_ERR_UNSUPPORTED); rows >= 0 (0 launches
+ *   nothing); x 16-byte aligned, codes 8-byte aligned.
+ */
+dsa_status_t dsa_index_rotate_quantize(const void* x, dsa_dtype_t x_dtype, int64_t rows, int32_t dim,
+                                       uint8_t* codes, uint8_t* scales, hipStream_t stream);
+
 #define DSA_OP_ATTN 1
 #define DSA_OP_FORWARD 2
 /* Workspace bytes needed by dsa_sparse_mla_attn (op = DSA_OP_ATTN) or

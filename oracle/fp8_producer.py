@@ -18,7 +18,8 @@ What it computes and where it comes from:
      "DeepSeek-V3.2-Exp" token-ids page gives "scale_fmt: ue8m0"; the drose
      page names F8_E4M3 as the FP8 format.  Reading: one power-of-two scale
      per row, the smallest 2^e with max|y| / 2^e <= 448 (the largest E4M3
-     value), stored as the byte e + 127 (an all-zero row uses e = 0); codes
+     value), stored as the byte e + 127 (an all-zero row uses e = 0; e is
+     clamped at -127, the byte's range, for rows below about 2^-118); codes
      are E4M3 ("fn": bias 7, no infinities) of y / 2^e, rounded to nearest
      with ties to even.
 
@@ -130,10 +131,12 @@ def e4m3_decode(c: np.ndarray) -> np.ndarray:
 
 
 def quantize_rows(y: np.ndarray):
-    """Per-row ue8m0 scale byte and E4M3 codes of rows y (last axis)."""
+    """Per-row ue8m0 scale byte and E4M3 codes of rows y (last axis).  The
+    exponent is clamped to the byte's range (e >= -127), which only matters
+    for rows whose maximum is below about 2^-118."""
     y = np.asarray(y, dtype=np.float64)
     amax = np.abs(y).max(axis=-1)
-    e = scale_exponent(amax)
+    e = np.clip(scale_exponent(amax), -127, 127)
     codes = e4m3_encode(y / np.exp2(e.astype(np.float64))[..., None])
     return codes, (e + 127).astype(np.uint8)
 

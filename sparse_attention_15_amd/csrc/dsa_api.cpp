@@ -296,6 +296,16 @@ int32_t dsa_forward_chunks(const dsa_problem_t* prob) {
   return plan_forward(*prob, path, true).n_chunks;
 }
 
+dsa_status_t dsa_index_rotate_quantize(const void* x, dsa_dtype_t x_dtype, int64_t rows, int32_t dim,
+                                       uint8_t* codes, uint8_t* scales, hipStream_t stream) {
+  if (rows < 0 || (x_dtype != DSA_BF16 && x_dtype != DSA_F32)) return DSA_ERR_INVALID_ARGUMENT;
+  if (dim != 128) return DSA_ERR_UNSUPPORTED;
+  if (rows == 0) return DSA_OK;
+  if (!x || !codes || !scales || !aligned16(x) || (reinterpret_cast<uintptr_t>(codes) & 7u))
+    return DSA_ERR_INVALID_ARGUMENT;
+  return hip_status(launch_rotate_quant(x, x_dtype == DSA_F32, rows, codes, scales, stream));
+}
+
 int32_t dsa_forward_attn_splits(const dsa_problem_t* prob) {
   Path path;
   if (check_problem(prob, &path) != DSA_OK) return 0;

@@ -99,10 +99,17 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
 // against readers of the destination with their own waits and barriers.
 #pragma clang diagnostic push
 #pragma clang diagnostic ignored "-Winline-asm"
+// NT: streaming (non-temporal) access for data read once.
+template <bool NT = true>
 __device__ __forceinline__ void lds_dma16(const void* gbase, uint32_t voff, uint32_t lds_base) {
-  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2 nt"
-               ::"s"(lds_base), "v"(voff), "s"(gbase)
-               : "m0");
+  if constexpr (NT)
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2 nt"
+                 ::"s"(lds_base), "v"(voff), "s"(gbase)
+                 : "m0");
+  else
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
+                 ::"s"(lds_base), "v"(voff), "s"(gbase)
+                 : "m0");
 }
 #pragma clang diagnostic pop
 

@@ -52,6 +52,10 @@ hipError_t launch_index_f32(const IndexLaunch& a, hipStream_t s);
 hipError_t launch_index_bf16(const IndexLaunch& a, hipStream_t s);
 hipError_t launch_index_fp8(const IndexLaunch& a, hipStream_t s);
 
+// FP8 producer: Hadamard rotation + ue8m0/E4M3 quantisation of 128-element rows.
+hipError_t launch_rotate_quant(const void* x, int f32_in, int64_t rows, uint8_t* codes, uint8_t* scales,
+                               hipStream_t s);
+
 // Top-k (all dtypes: scores are fp32).
 hipError_t launch_topk(const TopkLaunch& a, hipStream_t s);
 

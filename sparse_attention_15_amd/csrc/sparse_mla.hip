@@ -283,9 +283,11 @@ __global__ __launch_bounds__(kWavesA * 64, 1) void attn_bf16_kernel(AttnLaunch a
   const int j0 = split * per;
   const int nent = max(0, min(a.K, j0 + per) - j0);
 
-  // This split's list entries (all loads in flight at once), then the Q
-  // fragments; vector-memory completion is in order, so the list can be
-  // processed while the Q loads are still arriving.
+  // This split's list entries (all loads in flight at once), then the Q rows
+  // of this wave's 32 heads as one 32-row gather into a stage buffer (whole
+  // cache lines; read back with the key rows' conflict-free addressing):
+  // waves 0-2 now into buffers 0-2, wave 3 after the first barrier into
+  // buffer 2, while blocks 0 and 1 are gathered into buffers 0 and 1.
   constexpr int kFillIt = kMaxPer / (kWavesA * 64);
   int pv[kFillIt];
   const int32_t* idx = a.idx + qrow * a.K + j0;
@@ -296,11 +298,19 @@ __global__ __launch_bounds__(kWavesA * 64, 1) void attn_bf16_kernel(AttnLaunch a
   }
   AttnState st;
   const int h = 32 * wave + c32;
-  {
-    const uint8_t* qb = static_cast<const uint8_t*>(a.qa) + (qrow * kNH + h) * (int64_t)kRowB;
-#pragma unroll
-    for (int t = 0; t < kQSteps; ++t) st.qf[t] = ld16(qb + (16 * t + 8 * hf) * 2);
-  }
+  const uint8_t* qwave = static_cast<const uint8_t*>(a.qa) + (qrow * kNH + 32 * wave) * (int64_t)kRowB;  // uniform
+  const uint32_t stg_lds = lds_addr(stg);
+  auto gather_q = [&](int buf) {
+    const uint32_t dst = __builtin_amdgcn_readfirstlane(stg_lds + buf * kStageBytes);
+#pragma unroll 2
+    for (int k = 0; k < kDmaInstr; ++k) {
+      const int f = k * 64 + lane;
+      const int r = f / kLdsChunks, p = f - r * kLdsChunks;
+      const uint32_t off = (uint32_t)r * kRowB + (p < kChunks ? (uint32_t)((p ^ swz(r)) << 4) : 0u);
+      lds_dma16<false>(qwave, off, dst + k * 1024);
+    }
+  };
+  if (wave < 3) gather_q(wave);
   // Chosen rows into LDS as byte offsets (row * 1152; skipped and padding
   // entries point at row 0), one validity bit per entry in bmask (bit j of
   // word w: entry 32w + j is usable), and each wave's last usable entry.
@@ -339,6 +349,15 @@ __global__ __launch_bounds__(kWavesA * 64, 1) void attn_bf16_kernel(AttnLaunch a
 #pragma unroll
     for (int par = 0; par < 2; ++par) qk_off[par] = c32 * kLdsRow + 16 * ((2 * par + hf) ^ f);
   }
+  auto read_q = [&](int buf) {
+    const uint8_t* qbuf = stg + buf * kStageBytes;
+#pragma unroll
+    for (int t = 0; t < kQSteps; ++t) st.qf[t] = ld16(qbuf + qk_off[t & 1] + 64 * (t >> 1));
+  };
+  if (wave < 3) {
+    wait_vmcnt<0>();                              // this wave's Q rows have landed
+    read_q(wave);
+  }
   // PV operand (transposed reads) for 32x32x16: 16-lane group G holds value
   // rows 16(G&1) + j of the tile and k-half G>>1.  Step k, part w (lo/hi)
   // reads key row 16k + 8w + 4(G>>1) + j/4, value columns
@@ -360,11 +379,7 @@ __global__ __launch_bounds__(kWavesA * 64, 1) void attn_bf16_kernel(AttnLaunch a
   __syncthreads();
   const int last = max(max(s_lastw[0], s_lastw[1]), max(s_lastw[2], s_lastw[3]));
   const int nblk = (last + kBK) / kBK;            // blocks up to the last listed entry
-  // Consume the Q fragments here so that their loads are complete before the
-  // loop: the compiler's own vector-memory waits would otherwise stay inside
-  // the loop and also stall on the in-flight row gathers.
-#pragma unroll
-  for (int t = 0; t < kQSteps; ++t) asm volatile("" : "+v"(st.qf[t]));
+  if (wave == 3) gather_q(2);                     // wave 2 has read its Q from buffer 2
 
   // Gather map: instruction k of this wave fills LDS chunk slots
   // f = (dma_first(wave) + k)*64 + lane: row f/76, stored chunk f%76, which
@@ -384,7 +399,6 @@ __global__ __launch_bounds__(kWavesA * 64, 1) void attn_bf16_kernel(AttnLaunch a
     dma_map[k] = k >= dcount ? 0u : ((uint32_t)r | ((uint32_t)(p < kChunks ? (p ^ swz(r)) << 4 : 0) << 8));
   }
   const uint8_t* kvb = static_cast<const uint8_t*>(a.kv) + (int64_t)b * a.Lk * kRowB;   // uniform
-  const uint32_t stg_lds = lds_addr(stg);
   auto issue = [&](int blk, int sb) {
     const uint32_t dst = __builtin_amdgcn_readfirstlane(stg_lds + sb * kStageBytes);
     const uint32_t* bp = spos + blk * kBK;
@@ -401,6 +415,16 @@ __global__ __launch_bounds__(kWavesA * 64, 1) void attn_bf16_kernel(AttnLaunch a
   // block blk's QK steps.
   if (nblk > 0) issue(0, 0);
   if (nblk > 1) issue(1, 1);
+  if (wave == 3) {                                // Q rows are older than the block gathers
+    if (nblk > 1) wait_vmcnt<18>();
+    else if (nblk > 0) wait_vmcnt<9>();
+    else wait_vmcnt<0>();
+    read_q(2);
+  }
+  // Consume the Q fragments here so that their LDS reads are complete before
+  // the loop (block 2 is gathered into buffer 2 during block 0).
+#pragma unroll
+  for (int t = 0; t < kQSteps; ++t) asm volatile("" : "+v"(st.qf[t]));
   int sb = 0;
   Gather g;
   g.kvb = kvb;

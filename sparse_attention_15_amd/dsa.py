@@ -73,6 +73,9 @@ def lib() -> ctypes.CDLL:
     L.dsa_forward_chunks.restype = I32
     L.dsa_forward_attn_splits.argtypes = [P]
     L.dsa_forward_attn_splits.restype = I32
+    L.dsa_index_rotate_quantize.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_int32,
+                                            ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
+    L.dsa_index_rotate_quantize.restype = ctypes.c_int
     L.dsa_status_string.argtypes = [ctypes.c_int]
     L.dsa_status_string.restype = ctypes.c_char_p
     L.dsa_abi_version.argtypes = []
@@ -190,6 +193,27 @@ def forward_chunks(p: Problem) -> int:
 
 def attn_splits(p: Problem) -> int:
     return int(lib().dsa_forward_attn_splits(ctypes.byref(p)))
+
+
+def index_rotate_quantize(x: torch.Tensor, codes: torch.Tensor = None, scales: torch.Tensor = None):
+    """FP8 index vectors from bf16 / f32 activations: x [..., 128] ->
+    (codes uint8 [..., 128], scales uint8 [...]); see dsa_index_rotate_quantize."""
+    if x.dtype not in (torch.bfloat16, torch.float32):
+        raise DSAError(DSA_ERR_INVALID_ARGUMENT, "index_rotate_quantize: x must be bf16 or f32")
+    if not x.is_contiguous() or x.shape[-1] != 128 or not x.is_cuda:
+        raise DSAError(DSA_ERR_INVALID_ARGUMENT, "index_rotate_quantize: x must be a contiguous CUDA tensor [..., 128]")
+    rows = x.numel() // 128
+    if codes is None:
+        codes = torch.empty(x.shape, dtype=torch.uint8, device=x.device)
+    if scales is None:
+        scales = torch.empty(x.shape[:-1], dtype=torch.uint8, device=x.device)
+    if codes.dtype != torch.uint8 or codes.numel() != x.numel() or scales.dtype != torch.uint8 or scales.numel() != rows:
+        raise DSAError(DSA_ERR_INVALID_ARGUMENT, "index_rotate_quantize: output shapes / dtypes")
+    dt = DSA_F32 if x.dtype == torch.float32 else DSA_BF16
+    _check(lib().dsa_index_rotate_quantize(ctypes.c_void_p(x.data_ptr()), dt, rows, 128,
+                                           ctypes.c_void_p(codes.data_ptr()), ctypes.c_void_p(scales.data_ptr()),
+                                           _stream()), "dsa_index_rotate_quantize")
+    return codes, scales
 
 
 def _out_tensor(p: Problem, device):

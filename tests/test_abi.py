@@ -105,3 +105,15 @@ def test_invalid_arguments_are_rejected_before_launch(dsa):
     # timed forward: events requested but missing
     assert L.dsa_forward_timed(ctypes.byref(p), v, None, v, None, v, v, v, None, v, None, v, 1 << 40,
                                None, 8, None, None) == dsa.DSA_ERR_INVALID_ARGUMENT
+
+
+def test_rotate_quantize_rejects_bad_arguments_without_launching(dsa):
+    L = dsa.lib()
+    v = ctypes.c_void_p(16)
+    assert L.dsa_index_rotate_quantize(v, dsa.DSA_BF16, 0, 128, v, v, None) == dsa.DSA_OK      # nothing to do
+    assert L.dsa_index_rotate_quantize(v, dsa.DSA_BF16, -1, 128, v, v, None) == dsa.DSA_ERR_INVALID_ARGUMENT
+    assert L.dsa_index_rotate_quantize(v, dsa.DSA_BF16, 8, 64, v, v, None) == dsa.DSA_ERR_UNSUPPORTED
+    assert L.dsa_index_rotate_quantize(v, dsa.DSA_FP8_E4M3, 8, 128, v, v, None) == dsa.DSA_ERR_INVALID_ARGUMENT
+    assert L.dsa_index_rotate_quantize(None, dsa.DSA_BF16, 8, 128, v, v, None) == dsa.DSA_ERR_INVALID_ARGUMENT
+    assert L.dsa_index_rotate_quantize(ctypes.c_void_p(24), dsa.DSA_BF16, 8, 128, v, v, None) == \
+        dsa.DSA_ERR_INVALID_ARGUMENT

@@ -244,7 +244,7 @@ def _sample_rows(cfg, k):
 
 @pytest.mark.parametrize("cfg", [C.DECODE_32K, C.PREFILL_8K, C.DECODE_128K, C.PREFILL_64K_FP8], ids=lambda c: c.name)
 def test_full_size_sampled_rows(cfg):
-    """BASELINE-size workloads, same launch configuration as the bench, sampled rows vs the oracle."""
+    """Full-size workloads, same launch configuration as the bench, sampled rows vs the oracle."""
     inp = generate(cfg, device=DEV)
     out, lse, idx = _run_forward(cfg, inp)
     if cfg.q_len == 1:
