@@ -84,8 +84,8 @@ typedef struct {
  *   index BF16     + attn BF16 + out BF16|F32    H = 64, D = 128, NH = 128, Dqk = 576, Dv = 512
  *   index FP8_E4M3 + attn BF16 + out BF16|F32    same dims; q_scale/k_scale required
  * F32 limits: H*D <= 8192, Dqk <= 1024, Dv <= 1024, K <= 4096.
- * BF16 / FP8 limit: Lk <= 2^21 (latent rows are addressed with 32-bit byte
- * offsets within a sequence).
+ * BF16 / FP8 limits: Lk <= 2^21 (latent rows are addressed with 32-bit byte
+ * offsets within a sequence), K <= 65536.
  * All paths: K >= 1, Lq >= 1, Lk >= Lq, Lk <= 2^24 (scores rows in 32-bit indices).
  */
 

@@ -43,7 +43,8 @@ dsa_status_t check_problem(const dsa_problem_t* p, Path* path) {
     return DSA_OK;
   }
   if ((it == DSA_BF16 || it == DSA_FP8_E4M3) && at == DSA_BF16 && (ot == DSA_BF16 || ot == DSA_F32)) {
-    if (!is_v32_dims_index(*p) || !is_v32_dims_attn(*p) || p->kv_len > kMaxLkBf16) return DSA_ERR_UNSUPPORTED;
+    if (!is_v32_dims_index(*p) || !is_v32_dims_attn(*p) || p->kv_len > kMaxLkBf16 || p->topk > 65536)
+      return DSA_ERR_UNSUPPORTED;
     *path = it == DSA_BF16 ? kPathBF16 : kPathFP8;
     return DSA_OK;
   }

@@ -510,43 +510,50 @@ __global__ __launch_bounds__(kWavesA * 64, 1) void attn_bf16_kernel(AttnLaunch a
 }
 
 // Merge split partials: out = sum_s exp(lse_s - LSE) * O_s, LSE = log sum_s exp(lse_s).
-// grid (NH, rows), Dv/4 threads; partials in the output's precision.
+// grid (NH, rows), Dv/4 threads; partials in the output's precision.  S (the
+// split count, a power of two) is a template parameter so that all of a
+// thread's loads are in flight together.
+template <int S>
 __global__ __launch_bounds__(256) void attn_combine_kernel(AttnLaunch a) {
   const int h = blockIdx.x, rr = blockIdx.y, v = threadIdx.x * 4;
-  const int S = a.splits, NH = a.NH, Dv = a.Dv;
+  const int NH = a.NH, Dv = a.Dv;
   const int b = rr / a.q_count;
   const int i = a.q_begin + rr % a.q_count;
   const int64_t qrow = (int64_t)b * a.Lq + i;
   const float* pl = a.part_lse + (int64_t)rr * S * NH + h;
+  float ls[S];
+  f32x4 po[S];
+#pragma unroll
+  for (int s = 0; s < S; ++s) {
+    ls[s] = pl[(int64_t)s * NH];
+    const int64_t off = (((int64_t)rr * S + s) * NH + h) * Dv + v;
+    if (a.out_f32) {
+      po[s] = *reinterpret_cast<const f32x4*>(static_cast<const float*>(a.part_o) + off);
+    } else {
+      const u32x2 pb = *reinterpret_cast<const u32x2*>(static_cast<const uint16_t*>(a.part_o) + off);
+      po[s] = f32x4{bf16_lo(pb[0]), bf16_hi(pb[0]), bf16_lo(pb[1]), bf16_hi(pb[1])};
+    }
+  }
   float m = kNegInf;
-  for (int s = 0; s < S; ++s) m = fmaxf(m, pl[(int64_t)s * NH]);
+#pragma unroll
+  for (int s = 0; s < S; ++s) m = fmaxf(m, ls[s]);
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
   float sum = 0.f;
   if (m != kNegInf) {
+#pragma unroll
     for (int s = 0; s < S; ++s) {
-      const float ls = pl[(int64_t)s * NH];
-      if (ls == kNegInf) continue;
-      const float wgt = __expf(ls - m);
+      if (ls[s] == kNegInf) continue;             // an empty split holds zeros
+      const float wgt = __expf(ls[s] - m);
       sum += wgt;
-      const int64_t off = (((int64_t)rr * S + s) * NH + h) * Dv + v;
-      f32x4 po;
-      if (a.out_f32) {
-        po = *reinterpret_cast<const f32x4*>(static_cast<const float*>(a.part_o) + off);
-      } else {
-        const u32x2 pb = *reinterpret_cast<const u32x2*>(static_cast<const uint16_t*>(a.part_o) + off);
-        po = f32x4{bf16_lo(pb[0]), bf16_hi(pb[0]), bf16_lo(pb[1]), bf16_hi(pb[1])};
-      }
-      acc += wgt * po;
+      acc += wgt * po[s];
     }
     acc *= 1.f / sum;
   }
-  if (v < Dv) {
-    if (a.out_f32) {
-      *reinterpret_cast<f32x4*>(static_cast<float*>(a.out) + (qrow * NH + h) * Dv + v) = acc;
-    } else {
-      u32x2 v2 = {pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3])};
-      *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(a.out) + (qrow * NH + h) * Dv + v) = v2;
-    }
+  if (a.out_f32) {
+    *reinterpret_cast<f32x4*>(static_cast<float*>(a.out) + (qrow * NH + h) * Dv + v) = acc;
+  } else {
+    u32x2 v2 = {pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3])};
+    *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(a.out) + (qrow * NH + h) * Dv + v) = v2;
   }
   if (a.lse && threadIdx.x == 0) a.lse[qrow * NH + h] = m == kNegInf ? kNegInf : m + __logf(sum);
 }
@@ -615,8 +622,9 @@ __global__ __launch_bounds__(256) void attn_f32_kernel(AttnLaunch a) {
 int attn_splits_bf16(int rows, int K) {
   const int max_splits = (K + 63) / 64;           // at least 64 keys per split
   int s = 1;
-  while (rows * s < 256 && s * 2 <= max_splits) s *= 2;
-  // a split's list window lives in LDS: at most kMaxPer entries
+  while (rows * s < 256 && s * 2 <= max_splits && s < 32) s *= 2;
+  // a split's list window lives in LDS: at most kMaxPer entries (K <= 65536
+  // keeps this at 32 splits or fewer, the combine kernel's largest variant)
   while (((K + s - 1) / s + kBK - 1) / kBK * kBK > kMaxPer) s *= 2;
   return s;
 }
@@ -629,7 +637,15 @@ hipError_t launch_attn_bf16(const AttnLaunch& a, hipStream_t s) {
 
 hipError_t launch_attn_combine(const AttnLaunch& a, hipStream_t s) {
   dim3 grid(a.NH, a.B * a.q_count);
-  hipLaunchKernelGGL(attn_combine_kernel, grid, dim3(a.Dv / 4), 0, s, a);
+  dim3 block(a.Dv / 4);
+  switch (a.splits) {
+    case 2: hipLaunchKernelGGL(attn_combine_kernel<2>, grid, block, 0, s, a); break;
+    case 4: hipLaunchKernelGGL(attn_combine_kernel<4>, grid, block, 0, s, a); break;
+    case 8: hipLaunchKernelGGL(attn_combine_kernel<8>, grid, block, 0, s, a); break;
+    case 16: hipLaunchKernelGGL(attn_combine_kernel<16>, grid, block, 0, s, a); break;
+    case 32: hipLaunchKernelGGL(attn_combine_kernel<32>, grid, block, 0, s, a); break;
+    default: return hipErrorInvalidValue;       // splits are powers of two up to 32
+  }
   return hipGetLastError();
 }
 

@@ -91,6 +91,7 @@ def test_invalid_arguments_are_rejected_before_launch(dsa):
     assert _call_forward(dsa, _prob(dsa, C.DECODE_32K, index_heads=32)) == dsa.DSA_ERR_UNSUPPORTED
     assert _call_forward(dsa, _prob(dsa, C.DECODE_32K, index_dtype=dsa.DSA_F32)) == dsa.DSA_ERR_UNSUPPORTED
     assert _call_forward(dsa, _prob(dsa, C.DECODE_32K, kv_len=(1 << 21) + 1)) == dsa.DSA_ERR_UNSUPPORTED
+    assert _call_forward(dsa, _prob(dsa, C.DECODE_32K, topk=65537)) == dsa.DSA_ERR_UNSUPPORTED
     # fp8 without scales
     p8 = dsa.make_problem(C.PREFILL_64K_FP8)
     assert _call_forward(dsa, p8) == dsa.DSA_ERR_INVALID_ARGUMENT
