@@ -45,7 +45,7 @@
 extern "C" {
 #endif
 
-#define DSA_ABI_VERSION 1
+#define DSA_ABI_VERSION 2
 
 typedef enum {
   DSA_OK = 0,
@@ -77,6 +77,9 @@ typedef struct {
   dsa_dtype_t index_dtype;  /* q_idx / k_idx element type                     */
   dsa_dtype_t attn_dtype;   /* q_attn / kv element type                       */
   dsa_dtype_t out_dtype;    /* out element type                               */
+  int32_t kv_capacity;  /* tokens allocated per sequence in k_idx / k_scale / kv
+                           (the sequence stride of the caches); 0 means
+                           kv_len.  Must be 0 or >= kv_len.                  */
 } dsa_problem_t;
 
 /* Supported dtype combinations (anything else: DSA_ERR_UNSUPPORTED)
@@ -90,11 +93,13 @@ typedef struct {
  */
 
 /* Step 1: index scores.
+ *   Caches (k_idx, k_scale, kv) hold Lc = kv_capacity (or kv_len) tokens per
+ *   sequence; only the first Lk are read.
  *   q_idx   [B][Lq][H][D]  index_dtype (FP8: E4M3 codes, one byte each)
  *   q_scale [B][Lq][H]     uint8 ue8m0 exponents, scale = 2^(e-127); FP8 only,
  *                          else NULL.  One scale per 128-element row.
- *   k_idx   [B][Lk][D]     index_dtype, the single-head index-key cache
- *   k_scale [B][Lk]        uint8 ue8m0 exponents; FP8 only, else NULL
+ *   k_idx   [B][Lc][D]     index_dtype, the single-head index-key cache
+ *   k_scale [B][Lc]        uint8 ue8m0 exponents; FP8 only, else NULL
  *   head_w  [B][Lq][H]     fp32 per-query head weights (any sign)
  *   scores  [B][Lq][Lk]    fp32 out:
  *       scores[b][i][s] = sum_h w[h] * max(0, q_h . k_s)   for s <= p
@@ -123,7 +128,7 @@ dsa_status_t dsa_topk(const dsa_problem_t* prob, const float* scores, int64_t ro
 
 /* Step 3: sparse MLA attention over the chosen rows (absorbed MQA form).
  *   q_attn   [B][Lq][NH][Dqk] attn_dtype
- *   kv       [B][Lk][Dqk]     attn_dtype; one latent row per token, shared
+ *   kv       [B][Lc][Dqk]     attn_dtype; one latent row per token, shared
  *                             by all NH heads; values = its leading Dv dims
  *   topk_idx [B][Lq][K]       int32 positions; entries < 0 or >= Lk are
  *                             skipped, repeated entries count repeatedly; a
@@ -174,6 +179,23 @@ dsa_status_t dsa_forward_timed(const dsa_problem_t* prob,
                                hipEvent_t* events, int32_t n_events,
                                int32_t* n_chunks_out,
                                hipStream_t stream);
+
+/* Cache append (HF doc "DeepSeek-V3.2", section "DeepSeek Sparse Attention
+ * (DSA)": the indexer keeps its own cache of single-head index keys next to
+ * the MLA cache, filled as tokens are processed; update_indexer in the usage
+ * notes).  Writes n_new new tokens of every sequence into the caches at
+ * positions kv_len .. kv_len + n_new - 1, so that a following call with
+ * kv_len + n_new sees them.
+ *   k_new       [B][n_new][D]    index_dtype
+ *   k_new_scale [B][n_new]       uint8 ue8m0; FP8 index only, else NULL
+ *   kv_new      [B][n_new][Dqk]  attn_dtype
+ *   k_idx, k_scale, kv: the caches, [B][Lc][...] with Lc = kv_capacity,
+ *   which must be >= kv_len + n_new (kv_capacity 0 is rejected here).
+ *   Plain byte copies; n_new >= 0 (0 launches nothing).
+ */
+dsa_status_t dsa_cache_append(const dsa_problem_t* prob, int32_t n_new,
+                              const void* k_new, const uint8_t* k_new_scale, const void* kv_new,
+                              void* k_idx, uint8_t* k_scale, void* kv, hipStream_t stream);
 
 /* FP8 producer of the index vectors (HF doc "DeepSeek-V3.2", section
  * "DeepSeek Sparse Attention (DSA)", item 1: the indexer runs in FP8 after an

@@ -33,6 +33,7 @@ dsa_status_t check_problem(const dsa_problem_t* p, Path* path) {
   if (p->index_heads < 1 || p->index_dim < 1 || p->topk < 1) return DSA_ERR_INVALID_ARGUMENT;
   if (p->attn_heads < 1 || p->qk_dim < 1 || p->v_dim < 1 || p->v_dim > p->qk_dim) return DSA_ERR_INVALID_ARGUMENT;
   if (!std::isfinite(p->softmax_scale)) return DSA_ERR_INVALID_ARGUMENT;
+  if (p->kv_capacity != 0 && p->kv_capacity < p->kv_len) return DSA_ERR_INVALID_ARGUMENT;
   const int it = p->index_dtype, at = p->attn_dtype, ot = p->out_dtype;
   if (it < DSA_F32 || it > DSA_FP8_E4M3 || at < DSA_F32 || at > DSA_FP8_E4M3 || ot < DSA_F32 || ot > DSA_FP8_E4M3)
     return DSA_ERR_INVALID_ARGUMENT;
@@ -94,6 +95,7 @@ IndexLaunch make_index(const dsa_problem_t& p, const void* q, const uint8_t* qs,
   a.q = q; a.q_scale = qs; a.k = k; a.k_scale = ks; a.w = w;
   a.scores = scores; a.row_stride = row_stride;
   a.B = p.batch; a.Lq = p.q_len; a.Lk = p.kv_len; a.H = p.index_heads; a.D = p.index_dim;
+  a.Lc = p.kv_capacity ? p.kv_capacity : p.kv_len;
   a.q_begin = q_begin; a.q_count = q_count; a.write_masked = masked;
   return a;
 }
@@ -113,6 +115,7 @@ AttnLaunch make_attn(const dsa_problem_t& p, const void* qa, const void* kv, con
   AttnLaunch a;
   a.qa = qa; a.kv = kv; a.idx = idx; a.out = out; a.lse = lse;
   a.B = p.batch; a.Lq = p.q_len; a.Lk = p.kv_len; a.NH = p.attn_heads; a.Dqk = p.qk_dim; a.Dv = p.v_dim;
+  a.Lc = p.kv_capacity ? p.kv_capacity : p.kv_len;
   a.K = p.topk; a.q_begin = q_begin; a.q_count = q_count; a.splits = splits;
   a.scale = p.softmax_scale; a.out_f32 = p.out_dtype == DSA_F32;
   a.part_o = nullptr; a.part_lse = nullptr;
@@ -295,6 +298,27 @@ int32_t dsa_forward_chunks(const dsa_problem_t* prob) {
   Path path;
   if (check_problem(prob, &path) != DSA_OK) return 0;
   return plan_forward(*prob, path, true).n_chunks;
+}
+
+dsa_status_t dsa_cache_append(const dsa_problem_t* prob, int32_t n_new,
+                              const void* k_new, const uint8_t* k_new_scale, const void* kv_new,
+                              void* k_idx, uint8_t* k_scale, void* kv, hipStream_t stream) {
+  Path path;
+  const dsa_status_t st = check_problem(prob, &path);
+  if (st != DSA_OK) return st;
+  const dsa_problem_t& p = *prob;
+  if (n_new < 0 || p.kv_capacity == 0 || (int64_t)p.kv_len + n_new > p.kv_capacity) return DSA_ERR_INVALID_ARGUMENT;
+  if (n_new == 0) return DSA_OK;
+  const bool fp8 = path == kPathFP8;
+  if (!k_new || !kv_new || !k_idx || !kv || (fp8 && (!k_new_scale || !k_scale))) return DSA_ERR_INVALID_ARGUMENT;
+  const int kb = p.index_dim * (fp8 ? 1 : (p.index_dtype == DSA_F32 ? 4 : 2));
+  const int vb = p.qk_dim * (p.attn_dtype == DSA_F32 ? 4 : 2);
+  CacheAppend c;
+  c.B = p.batch; c.n_new = n_new; c.pos = p.kv_len; c.cap = p.kv_capacity;
+  c.k_new = k_new; c.ks_new = fp8 ? k_new_scale : nullptr; c.kv_new = kv_new;
+  c.k = k_idx; c.ks = fp8 ? k_scale : nullptr; c.kv = kv;
+  c.k_row_bytes = kb; c.kv_row_bytes = vb;
+  return hip_status(launch_cache_append(c, stream));
 }
 
 dsa_status_t dsa_index_rotate_quantize(const void* x, dsa_dtype_t x_dtype, int64_t rows, int32_t dim,

@@ -18,6 +18,7 @@ struct IndexLaunch {
   float* scores;           // rows of row_stride floats
   int64_t row_stride;
   int B, Lq, Lk, H, D;
+  int Lc;                  // tokens per sequence in the key caches (>= Lk)
   int q_begin, q_count;
   int write_masked;        // also write -inf for positions beyond the causal limit
 };
@@ -33,7 +34,7 @@ struct TopkLaunch {
 
 struct AttnLaunch {
   const void* qa;          // [B][Lq][NH][Dqk]
-  const void* kv;          // [B][Lk][Dqk]
+  const void* kv;          // [B][Lc][Dqk]
   const int32_t* idx;      // [B][Lq][K] (full-tensor numbering)
   void* out;               // [B][Lq][NH][Dv]
   float* lse;              // [B][Lq][NH] or null
@@ -41,6 +42,7 @@ struct AttnLaunch {
                            // output's precision: fp32 for fp32 out, bf16 for bf16 out
   float* part_lse;         // [rows][S][NH]
   int B, Lq, Lk, NH, Dqk, Dv, K;
+  int Lc;                  // tokens per sequence in the latent cache (>= Lk)
   int q_begin, q_count;
   int splits;              // S: key ranges per query (1 = no combine step)
   float scale;
@@ -51,6 +53,15 @@ struct AttnLaunch {
 hipError_t launch_index_f32(const IndexLaunch& a, hipStream_t s);
 hipError_t launch_index_bf16(const IndexLaunch& a, hipStream_t s);
 hipError_t launch_index_fp8(const IndexLaunch& a, hipStream_t s);
+
+// Cache append: rows of n_new tokens per sequence copied to positions pos..
+struct CacheAppend {
+  int B, n_new, pos, cap;
+  const void* k_new; const uint8_t* ks_new; const void* kv_new;
+  void* k; uint8_t* ks; void* kv;
+  int k_row_bytes, kv_row_bytes;
+};
+hipError_t launch_cache_append(const CacheAppend& c, hipStream_t s);
 
 // FP8 producer: Hadamard rotation + ue8m0/E4M3 quantisation of 128-element rows.
 hipError_t launch_rotate_quant(const void* x, int f32_in, int64_t rows, uint8_t* codes, uint8_t* scales,

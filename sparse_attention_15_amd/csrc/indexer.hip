@@ -52,7 +52,7 @@ __global__ __launch_bounds__(256) void idx_f32_kernel(IndexLaunch a) {
     if (a.write_masked) out[s] = kNegInf;
     return;
   }
-  const float* kr = static_cast<const float*>(a.k) + ((int64_t)b * a.Lk + s) * D;
+  const float* kr = static_cast<const float*>(a.k) + ((int64_t)b * a.Lc + s) * D;
   float acc = 0.f;
   for (int h = 0; h < H; ++h) {
     float x = 0.f;
@@ -113,22 +113,6 @@ __device__ __forceinline__ void load_query(const IndexLaunch& a, int64_t qrow, i
       if constexpr (FP8) wh *= ue8m0_to_f32(a.q_scale[qrow * kH + h]);
       wv[4 * m + j] = wh;
     }
-}
-
-// Key fragments of the 16-key tile starting at key k0 (rows past the end are
-// clamped to the last row; their scores are never stored).
-template <bool FP8>
-__device__ __forceinline__ void load_keys_global(const uint8_t* kbase, int k0, int Lk, int lane, KFrag<FP8>& kf) {
-  const int r = lane & 15, g = lane >> 4;
-  const int key = min(k0 + r, Lk - 1);
-  if constexpr (!FP8) {
-    const uint8_t* p = kbase + (int64_t)key * (kD * 2) + 16 * g;
-#pragma unroll
-    for (int t = 0; t < 4; ++t) kf.v[t] = ld16_stream(p + 64 * t);
-  } else {
-    const uint8_t* p = kbase + (int64_t)key * kD + 32 * g;
-    kf.v = join(ld16_stream(p), ld16_stream(p + 16));
-  }
 }
 
 // Scores of one 16-key tile for one query: returns the score of key r in
@@ -204,7 +188,7 @@ __global__ __launch_bounds__(256, 2) void idx_decode_kernel(IndexLaunch a) {
   const int nst = (nk + TK - 1) / TK;
 
   const int64_t qrow = (int64_t)b * a.Lq + i;
-  const uint8_t* kbase = static_cast<const uint8_t*>(a.k) + (int64_t)b * a.Lk * ROWB;   // wave-uniform
+  const uint8_t* kbase = static_cast<const uint8_t*>(a.k) + (int64_t)b * a.Lc * ROWB;   // wave-uniform
 
   // copy k of a stage fills LDS slots 64k + lane: row slot/CPR, stored
   // position slot%CPR, holding global chunk position ^ (row % CPR)
@@ -230,7 +214,7 @@ __global__ __launch_bounds__(256, 2) void idx_decode_kernel(IndexLaunch a) {
   for (int st = 0; st < kDecRing - 1; ++st)
     if (st < nst) issue(st);
   if constexpr (FP8) {
-    const uint8_t* ks = a.k_scale + (int64_t)b * a.Lk;
+    const uint8_t* ks = a.k_scale + (int64_t)b * a.Lc;
     for (int j = lane; j < nk; j += 64) kscale[wave][j] = ks[w0 + j];
   }
   QFrag<FP8> q;
@@ -312,8 +296,8 @@ __global__ __launch_bounds__(QB * 64) void idx_prefill_kernel(IndexLaunch a, int
   const int ntiles = (n_max + TK - 1) / TK;
   const int row = b * a.q_count + ii;
   float* out = a.scores + (int64_t)row * a.row_stride;
-  const uint8_t* kbase = static_cast<const uint8_t*>(a.k) + (int64_t)b * a.Lk * ROWB;   // uniform
-  const uint8_t* ks = FP8 ? a.k_scale + (int64_t)b * a.Lk : nullptr;
+  const uint8_t* kbase = static_cast<const uint8_t*>(a.k) + (int64_t)b * a.Lc * ROWB;   // uniform
+  const uint8_t* ks = FP8 ? a.k_scale + (int64_t)b * a.Lc : nullptr;
 
   // this block's tiles: kt = blockIdx.y + ksplit * j, j < nj
   const int nj = blockIdx.y < ntiles ? (ntiles - 1 - blockIdx.y) / ksplit + 1 : 0;

@@ -398,7 +398,7 @@ __global__ __launch_bounds__(kWavesA * 64, 1) void attn_bf16_kernel(AttnLaunch a
     const int r = f / kLdsChunks, p = f - r * kLdsChunks;
     dma_map[k] = k >= dcount ? 0u : ((uint32_t)r | ((uint32_t)(p < kChunks ? (p ^ swz(r)) << 4 : 0) << 8));
   }
-  const uint8_t* kvb = static_cast<const uint8_t*>(a.kv) + (int64_t)b * a.Lk * kRowB;   // uniform
+  const uint8_t* kvb = static_cast<const uint8_t*>(a.kv) + (int64_t)b * a.Lc * kRowB;   // uniform
   auto issue = [&](int blk, int sb) {
     const uint32_t dst = __builtin_amdgcn_readfirstlane(stg_lds + sb * kStageBytes);
     const uint32_t* bp = spos + blk * kBK;
@@ -572,7 +572,7 @@ __global__ __launch_bounds__(256) void attn_f32_kernel(AttnLaunch a) {
   const int i = a.q_begin + rr % a.q_count;
   const int64_t qrow = (int64_t)b * a.Lq + i;
   const float* qg = static_cast<const float*>(a.qa) + (qrow * NH + h) * Dqk;
-  const float* kvb = static_cast<const float*>(a.kv) + (int64_t)b * a.Lk * Dqk;
+  const float* kvb = static_cast<const float*>(a.kv) + (int64_t)b * a.Lc * Dqk;
   const int32_t* idx = a.idx + qrow * K;
   for (int d = tid; d < Dqk; d += 256) qs[d] = qg[d];
   __syncthreads();

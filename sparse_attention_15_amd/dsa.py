@@ -39,6 +39,7 @@ class Problem(ctypes.Structure):
         ("attn_heads", ctypes.c_int32), ("qk_dim", ctypes.c_int32), ("v_dim", ctypes.c_int32),
         ("softmax_scale", ctypes.c_float),
         ("index_dtype", ctypes.c_int), ("attn_dtype", ctypes.c_int), ("out_dtype", ctypes.c_int),
+        ("kv_capacity", ctypes.c_int32),
     ]
 
 
@@ -76,6 +77,8 @@ def lib() -> ctypes.CDLL:
     L.dsa_index_rotate_quantize.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_int32,
                                             ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
     L.dsa_index_rotate_quantize.restype = ctypes.c_int
+    L.dsa_cache_append.argtypes = [P, ctypes.c_int32] + [ctypes.c_void_p] * 6 + [ctypes.c_void_p]
+    L.dsa_cache_append.restype = ctypes.c_int
     L.dsa_status_string.argtypes = [ctypes.c_int]
     L.dsa_status_string.restype = ctypes.c_char_p
     L.dsa_abi_version.argtypes = []
@@ -109,12 +112,17 @@ class Shape:
     out_dtype: str
 
 
-def make_problem(cfg, out_dtype: str | None = None) -> Problem:
-    """Problem from any object with the DSAConfig field names."""
+def make_problem(cfg, out_dtype: str | None = None, kv_capacity: int = 0) -> Problem:
+    """Problem from any object with the DSAConfig field names; kv_capacity is
+    the caches' tokens per sequence (0: kv_len)."""
     od = out_dtype or cfg.attn_dtype
     return Problem(cfg.batch, cfg.q_len, cfg.kv_len, cfg.index_heads, cfg.index_dim, cfg.topk,
                    cfg.attn_heads, cfg.qk_dim, cfg.v_dim, float(cfg.softmax_scale),
-                   _DTYPE_CODE[cfg.index_dtype], _DTYPE_CODE[cfg.attn_dtype], _DTYPE_CODE[od])
+                   _DTYPE_CODE[cfg.index_dtype], _DTYPE_CODE[cfg.attn_dtype], _DTYPE_CODE[od], kv_capacity)
+
+
+def _cap(p: Problem) -> int:
+    return p.kv_capacity if p.kv_capacity else p.kv_len
 
 
 def _stream() -> ctypes.c_void_p:
@@ -153,8 +161,8 @@ def _index_args(p: Problem, q_idx, q_scale, k_idx, k_scale, head_w):
     fp8 = p.index_dtype == DSA_FP8_E4M3
     return (_ptr(q_idx, "q_idx", it, (B, Lq, H, D)),
             _ptr(q_scale, "q_scale", torch.uint8, (B, Lq, H), allow_none=not fp8),
-            _ptr(k_idx, "k_idx", it, (B, Lk, D)),
-            _ptr(k_scale, "k_scale", torch.uint8, (B, Lk), allow_none=not fp8),
+            _ptr(k_idx, "k_idx", it, (B, _cap(p), D)),
+            _ptr(k_scale, "k_scale", torch.uint8, (B, _cap(p)), allow_none=not fp8),
             _ptr(head_w, "head_w", torch.float32, (B, Lq, H)))
 
 
@@ -195,6 +203,22 @@ def attn_splits(p: Problem) -> int:
     return int(lib().dsa_forward_attn_splits(ctypes.byref(p)))
 
 
+def cache_append(p: Problem, k_new, k_new_scale, kv_new, k_idx, k_scale, kv):
+    """Append n_new tokens per sequence at positions p.kv_len.. of the caches
+    (k_new [B, n_new, D], kv_new [B, n_new, Dqk]; caches [B, kv_capacity, ...])."""
+    B = p.batch
+    n_new = k_new.shape[1]
+    it, at = _TORCH_DT[p.index_dtype], _TORCH_DT[p.attn_dtype]
+    fp8 = p.index_dtype == DSA_FP8_E4M3
+    args = (_ptr(k_new, "k_new", it, (B, n_new, p.index_dim)),
+            _ptr(k_new_scale, "k_new_scale", torch.uint8, (B, n_new), allow_none=not fp8),
+            _ptr(kv_new, "kv_new", at, (B, n_new, p.qk_dim)),
+            _ptr(k_idx, "k_idx", it, (B, _cap(p), p.index_dim)),
+            _ptr(k_scale, "k_scale", torch.uint8, (B, _cap(p)), allow_none=not fp8),
+            _ptr(kv, "kv", at, (B, _cap(p), p.qk_dim)))
+    _check(lib().dsa_cache_append(ctypes.byref(p), n_new, *args, _stream()), "dsa_cache_append")
+
+
 def index_rotate_quantize(x: torch.Tensor, codes: torch.Tensor = None, scales: torch.Tensor = None):
     """FP8 index vectors from bf16 / f32 activations: x [..., 128] ->
     (codes uint8 [..., 128], scales uint8 [...]); see dsa_index_rotate_quantize."""
@@ -226,7 +250,7 @@ def _attn_args(p: Problem, q_attn, kv, out, lse):
     at = _TORCH_DT[p.attn_dtype]
     ot = torch.float32 if p.out_dtype == DSA_F32 else torch.bfloat16
     return (_ptr(q_attn, "q_attn", at, (B, Lq, p.attn_heads, p.qk_dim)),
-            _ptr(kv, "kv", at, (B, Lk, p.qk_dim)),
+            _ptr(kv, "kv", at, (B, _cap(p), p.qk_dim)),
             _ptr(out, "out", ot, (B, Lq, p.attn_heads, p.v_dim)),
             _ptr(lse, "lse", torch.float32, (B, Lq, p.attn_heads), allow_none=True))
 

@@ -37,7 +37,7 @@ def test_library_exports_every_declared_symbol(dsa):
     L = dsa.lib()
     for name in _declared_functions():
         assert hasattr(L, name), name
-    assert dsa.abi_version() == 1
+    assert dsa.abi_version() == 2
 
 
 def test_status_strings(dsa):
@@ -118,3 +118,17 @@ def test_rotate_quantize_rejects_bad_arguments_without_launching(dsa):
     assert L.dsa_index_rotate_quantize(None, dsa.DSA_BF16, 8, 128, v, v, None) == dsa.DSA_ERR_INVALID_ARGUMENT
     assert L.dsa_index_rotate_quantize(ctypes.c_void_p(24), dsa.DSA_BF16, 8, 128, v, v, None) == \
         dsa.DSA_ERR_INVALID_ARGUMENT
+
+
+def test_cache_append_checks_capacity_without_launching(dsa):
+    L = dsa.lib()
+    v = ctypes.c_void_p(16)
+    p = dsa.make_problem(C.DECODE_32K, kv_capacity=32768)          # full: no room
+    assert L.dsa_cache_append(ctypes.byref(p), 1, v, None, v, v, None, v, None) == dsa.DSA_ERR_INVALID_ARGUMENT
+    assert L.dsa_cache_append(ctypes.byref(p), 0, v, None, v, v, None, v, None) == dsa.DSA_OK
+    p0 = dsa.make_problem(C.DECODE_32K)                            # capacity 0: nothing to append into
+    assert L.dsa_cache_append(ctypes.byref(p0), 1, v, None, v, v, None, v, None) == dsa.DSA_ERR_INVALID_ARGUMENT
+    small = dsa.make_problem(C.DECODE_32K, kv_capacity=100)        # capacity below kv_len
+    assert _call_forward(dsa, small) == dsa.DSA_ERR_INVALID_ARGUMENT
+    room = dsa.make_problem(C.DECODE_32K, kv_capacity=40000)
+    assert L.dsa_cache_append(ctypes.byref(room), 4, v, None, None, v, None, v, None) == dsa.DSA_ERR_INVALID_ARGUMENT
