@@ -187,6 +187,88 @@ def copy_calibration(nbytes=1 << 30, reps=5):
                       "copy_GBps_read_plus_write": round(2 * nbytes / el / 1e9, 1)}), flush=True)
 
 
+def decode_loop(args, cfg, dsa, generate, torch):
+    """Multi-step decode with cache appends: contexts L0+1 .. Lk, one query per
+    sequence per step."""
+    from dsa_workloads import scaled
+    if cfg.q_len != 1:
+        print("--decode-loop applies to decode workloads (one query per sequence)", file=sys.stderr)
+        sys.exit(2)
+    N = args.steps
+    L0 = cfg.kv_len - N
+    # the full caches at the final context, and N queries: step t is row t of
+    # the causal problem with Lq = N, Lk = L0 + N
+    full = generate(scaled(cfg, q_len=N), device="cuda:0")
+    B, cap = cfg.batch, cfg.kv_len
+    k_c = full["k_idx"].clone()
+    ks_c = full["k_scale"].clone() if full["k_scale"] is not None else None
+    kv_c = full["kv"].clone()
+    new_k = [full["k_idx"][:, L0 + t:L0 + t + 1].contiguous() for t in range(N)]
+    new_ks = [full["k_scale"][:, L0 + t:L0 + t + 1].contiguous() if ks_c is not None else None for t in range(N)]
+    new_kv = [full["kv"][:, L0 + t:L0 + t + 1].contiguous() for t in range(N)]
+    qs = {k: [full[k][:, t:t + 1].contiguous() if full[k] is not None else None for t in range(N)]
+          for k in ("q_idx", "q_scale", "head_w", "q_attn")}
+    probs_app = [dsa.make_problem(scaled(cfg, kv_len=L0 + t), kv_capacity=cap) for t in range(N)]
+    probs_fwd = [dsa.make_problem(scaled(cfg, kv_len=L0 + t + 1), kv_capacity=cap) for t in range(N)]
+    ws = torch.empty(max(dsa.workspace_size(pp, dsa.DSA_OP_FORWARD) for pp in probs_fwd), dtype=torch.uint8,
+                     device="cuda:0")
+    odt = torch.float32 if probs_fwd[0].out_dtype == dsa.DSA_F32 else torch.bfloat16
+    out = torch.empty(B, 1, cfg.attn_heads, cfg.v_dim, dtype=odt, device="cuda:0")
+    lse = torch.empty(B, 1, cfg.attn_heads, dtype=torch.float32, device="cuda:0")
+    ev = []
+
+    def run(record):
+        for t in range(N):
+            if record:
+                e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+                e[0].record()
+            dsa.cache_append(probs_app[t], new_k[t], new_ks[t], new_kv[t], k_c, ks_c, kv_c)
+            if record:
+                e[1].record()
+            dsa.forward(probs_fwd[t], qs["q_idx"][t], qs["q_scale"][t], k_c, ks_c, qs["head_w"][t],
+                        qs["q_attn"][t], kv_c, out=out, lse=lse, workspace=ws)
+            if record:
+                e[2].record()
+                ev.append(e)
+
+    for _ in range(max(1, args.warmup // max(1, N))):
+        run(False)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    run(False)
+    torch.cuda.synchronize()
+    el = time.perf_counter() - t0
+    run(True)
+    torch.cuda.synchronize()
+    app = [e[0].elapsed_time(e[1]) for e in ev]
+    fwd = [e[1].elapsed_time(e[2]) for e in ev]
+    ms = el * 1e3 / N
+    res = {
+        "metric": "DSA queries/sec (indexer+top-k+sparse MLA)",
+        "value": round(B * N / el, 1),
+        "unit": "queries/s",
+        "n_gpus": 1,
+        "steps": N,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": {"bf16": "bf16", "f32": "f32", "fp8_e4m3": "fp8_e4m3+bf16"}[cfg.index_dtype],
+        "data": "synthetic (seeded generators; no dataset or weights)",
+        "config": {"workload": cfg.name + "+decode_loop", "batch": B, "q_len": 1,
+                   "start_context": L0 + 1, "end_context": L0 + N, "kv_capacity": cap,
+                   "index_heads": cfg.index_heads, "index_dim": cfg.index_dim, "topk": cfg.topk,
+                   "attn_heads": cfg.attn_heads, "qk_dim": cfg.qk_dim, "v_dim": cfg.v_dim},
+        "decode_loop": {"append_us_mean": round(1e3 * sum(app) / N, 2),
+                        "forward_ms_first": round(fwd[0], 5), "forward_ms_last": round(fwd[-1], 5),
+                        "forward_ms_mean": round(sum(fwd) / N, 5),
+                        "note": "each step: append one token per sequence (index key + latent row), then "
+                                "one query per sequence at the grown context; events bracket each call"},
+    }
+    print(json.dumps(res), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -199,6 +281,10 @@ def main():
     ap.add_argument("--with-producer", action="store_true",
                     help="FP8-index workloads: start each step from bf16 index activations and run the FP8 "
                          "producer (Hadamard rotation + ue8m0/E4M3 quantisation) before the fused path")
+    ap.add_argument("--decode-loop", action="store_true",
+                    help="decode workloads: each step appends one token per sequence to caches with room for "
+                         "them and runs the fused path for one query at the grown context; the `steps` "
+                         "steps end at the workload's context")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a 1 GiB elementwise copy (for calibrating rocprofv3 byte counters)")
     args = ap.parse_args()
@@ -217,6 +303,9 @@ def main():
     cfg = BY_NAME[args.config]
     dev = "cuda:0"
     torch.cuda.set_device(0)
+    if args.decode_loop:
+        decode_loop(args, cfg, dsa, generate, torch)
+        return
     p = dsa.make_problem(cfg, out_dtype=args.out_dtype)
     nsets = max(1, args.sets if cfg.q_len <= 4 else min(args.sets, 2))
     producer = args.with_producer
