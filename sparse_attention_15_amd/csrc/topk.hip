@@ -10,13 +10,22 @@
 // One work-group per row.  Scores become order-preserving 32-bit keys; an
 // MSB-first radix select (12 + 12 + 8 bits, LDS histograms) finds the
 // threshold key T and how many elements equal to T are still needed (r).
-// The selection is then {key > T} plus the first r positions with key == T,
-// and one ordered pass writes it: for a chosen element at position x its
-// output slot is  #(key > T before x) + min(#(key == T before x), r),
-// so block-wide scans of packed (gt, eq) counts give the slots (DPP wave
-// scans, one barrier per group of 8 chunks).
-// Row values stay in registers (4 consecutive positions per 16-byte load);
-// rows longer than the register budget are re-read from memory each pass.
+// Index scores crowd into a few exponents, so many lanes of one atomic
+// instruction hit the same bin; each histogram therefore keeps C copies
+// (lane l adds to copy l % C), laid out copy-major with a stride of 4096 + 4
+// words so the copies of one bin sit in different banks and a thread's run
+// of 4 bins is one aligned 16-byte read.
+// The selection is {key > T} plus the first r positions with key == T.
+// Rows held in registers (4 consecutive positions per 16-byte load) write
+// two bitmaps over positions, "above T" and "equal to T", one 32-position
+// word per 8 lanes (DPP OR of their 4-bit groups); one thread per word then
+// turns a block-wide scan of the word counts into output slots, keeping the
+// equal positions while fewer than r came before, and writes the positions
+// of its set bits.  Longer rows, re-read from memory each pass, use an
+// ordered pass over the elements instead: for a chosen element at position
+// x its slot is  #(key > T before x) + min(#(key == T before x), r), from
+// block-wide scans of packed counts (one barrier per group of 8 chunks).
+// Slots go to LDS first and leave in one coalesced copy (K <= 4096).
 #include "dsa_device.h"
 #include "dsa_internal.h"
 
@@ -25,6 +34,8 @@ namespace {
 
 constexpr int kThreads = 1024;
 constexpr int kWaves = kThreads / 64;
+constexpr int kBins = 4096;
+constexpr int kGroup = 8;            // chunks per emission group
 
 __device__ __forceinline__ uint32_t order_key(float x) {
   uint32_t u = __builtin_bit_cast(uint32_t, x);
@@ -42,7 +53,7 @@ __device__ __forceinline__ uint32_t dpp(uint32_t v) {
 // 16 lanes, then row 0's total into row 1 and row 2's into row 3
 // (row_bcast:15), then lane 31's running total into rows 2 and 3
 // (row_bcast:31).
-__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t v, int) {
+__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t v) {
   v += dpp<0x111, 0xf>(v);
   v += dpp<0x112, 0xf>(v);
   v += dpp<0x114, 0xf>(v);
@@ -52,49 +63,76 @@ __device__ __forceinline__ uint32_t wave_incl_scan(uint32_t v, int) {
   return v;
 }
 
-constexpr int kGroup = 8;            // chunks per emission group
-
+template <int NC, int C>
 struct Shared {
-  uint32_t hist[4096];
+  static constexpr int kStride = kBins + 4;   // bin j, copy c at c * kStride + j
+  static constexpr int kWords = NC > 0 ? NC * kThreads * 4 / 32 : 1;   // bitmap words
+  alignas(16) uint32_t hist[C * kStride];   // histograms; at the end the output stage
+  uint32_t gt_bits[kWords];         // position x: bit x % 32 of word x / 32
+  uint32_t eq_bits[kWords];
   uint32_t wsum[kGroup * kWaves];
-  uint32_t bin;        // chosen bin of the current pass
-  uint32_t above;      // elements in bins above it
+  uint32_t bin;                     // chosen bin of the current pass
+  uint32_t above;                   // elements in bins above it
+  uint32_t cnt;                     // elements in it
 };
 
-// Find the bin holding the k-th largest element (k >= 1) of hist[0..nb).
-// Thread t owns a run of bins counted from the top, so a block-wide scan of
-// the per-thread sums gives each run the number of elements above it.
-// Returns via sh.bin / sh.above.  All threads must call.
-__device__ void find_bin(Shared& sh, int nb, uint32_t k) {
+// Find the bin holding the k-th largest element (k >= 1) of a histogram of
+// nb bins (4096 or 256).  Thread t owns a run of bins counted from the top,
+// so a block-wide scan of the per-thread sums gives each run the number of
+// elements above it.  Returns via sh.bin / sh.above / sh.cnt.  All threads
+// must call.
+template <int NC, int C>
+__device__ void find_bin(Shared<NC, C>& sh, int nb, uint32_t k) {
+  constexpr int S = Shared<NC, C>::kStride;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int per = nb >= kThreads ? nb / kThreads : 1;
-  const int hi = nb - per * tid;                 // my bins: [hi - per, hi)
-  uint32_t local = 0;
-  if (hi > 0)
-    for (int j = 1; j <= per; ++j) local += sh.hist[hi - j];
-  const uint32_t incl = wave_incl_scan(local, lane);
+  uint32_t c4[4] = {0u, 0u, 0u, 0u};             // my bins, highest first
+  int top;                                       // my highest bin
+  int per;
+  if (nb == 4 * kThreads) {                      // 4 bins: one 16-byte read per copy
+    per = 4;
+    top = nb - 1 - 4 * tid;
+#pragma unroll
+    for (int r = 0; r < C; ++r) {
+      const u32x4 v = *reinterpret_cast<const u32x4*>(&sh.hist[r * S + top - 3]);
+      c4[0] += v.w;
+      c4[1] += v.z;
+      c4[2] += v.y;
+      c4[3] += v.x;
+    }
+  } else {                                       // nb <= kThreads: one bin
+    per = 1;
+    top = nb - 1 - tid;
+    if (top >= 0)
+#pragma unroll
+      for (int r = 0; r < C; ++r) c4[0] += sh.hist[r * S + top];
+  }
+  const uint32_t local = c4[0] + c4[1] + c4[2] + c4[3];
+  const uint32_t incl = wave_incl_scan(local);
   if (lane == 63) sh.wsum[wave] = incl;
   __syncthreads();
   uint32_t before = 0;
   for (int w = 0; w < wave; ++w) before += sh.wsum[w];
   uint32_t run = before + incl - local;          // count strictly above my bins
   if (run < k && run + local >= k) {
-    for (int j = 1; j <= per; ++j) {
-      const uint32_t c = sh.hist[hi - j];
-      if (run + c >= k) {
-        sh.bin = hi - j;
+    for (int j = 0; j < per; ++j) {
+      if (run + c4[j] >= k) {
+        sh.bin = top - j;
         sh.above = run;
+        sh.cnt = c4[j];
         break;
       }
-      run += c;
+      run += c4[j];
     }
   }
   __syncthreads();
 }
 
-template <int NC>  // NC 16-byte chunks per thread kept in registers; 0 = stream
+// NC 16-byte chunks per thread kept in registers (0 = re-read each pass);
+// C histogram copies.
+template <int NC, int C>
 __global__ __launch_bounds__(kThreads) void topk_kernel(TopkLaunch a) {
-  __shared__ Shared sh;
+  __shared__ Shared<NC, C> sh;
+  constexpr int S = Shared<NC, C>::kStride;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int row = gridDim.x - 1 - blockIdx.x;     // longest rows first
   const int b = row / a.q_count;
@@ -140,14 +178,19 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(TopkLaunch a) {
   uint32_t prefix = 0, mask = 0, k_rem = (uint32_t)K;
   const int shifts[3] = {20, 8, 0};
   const int widths[3] = {12, 12, 8};
+  const uint32_t copy_base = (uint32_t)(lane & (C - 1)) * S;
   for (int pass = 0; pass < 3; ++pass) {
     const int sh_ = shifts[pass], nb = 1 << widths[pass];
-    for (int j = tid; j < nb; j += kThreads) sh.hist[j] = 0;
+    for (int j = tid; j < C * nb / 4; j += kThreads) {
+      const int r = j / (nb / 4), o = j - r * (nb / 4);
+      st16(&sh.hist[r * S + 4 * o], u32x4{0u, 0u, 0u, 0u});
+    }
     __syncthreads();
     auto count = [&](const uint32_t (&kk)[4]) {
 #pragma unroll
       for (int e = 0; e < 4; ++e)
-        if ((kk[e] & mask) == prefix && kk[e] != 0u) atomicAdd(&sh.hist[(kk[e] >> sh_) & (nb - 1)], 1u);
+        if ((kk[e] & mask) == prefix && kk[e] != 0u)
+          atomicAdd(&sh.hist[copy_base + ((kk[e] >> sh_) & (nb - 1))], 1u);
     };
     if constexpr (NC > 0) {
 #pragma unroll
@@ -163,82 +206,170 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(TopkLaunch a) {
     __syncthreads();
     find_bin(sh, nb, k_rem);
     const uint32_t bin = sh.bin;
-    const uint32_t cnt = sh.hist[bin];
+    const uint32_t cnt = sh.cnt;
     k_rem -= sh.above;
     prefix |= bin << sh_;
     mask |= (uint32_t)(nb - 1) << sh_;
-    __syncthreads();
     if (cnt == k_rem) break;                      // the whole bin is taken
   }
+  // hist is free from here on (the last find_bin ended with a barrier and
+  // nothing reads it after): it becomes the output stage.
+  const bool staged = K <= kBins;
+  auto put = [&](uint32_t slot, int pos) {
+    if (slot < (uint32_t)K) {                     // always, by construction
+      if (staged) sh.hist[slot] = (uint32_t)pos;
+      else out[slot] = pos;
+    }
+  };
 
-  // Ordered emission: chunk c holds positions 4*(c*kThreads + tid) + 0..3,
-  // so positions run over (chunk, thread, element).  A group of chunks is
-  // scanned at once (one barrier): per chunk a block-wide exclusive scan of
-  // the packed (gt, eq) counts, plus running totals over earlier chunks.
-  uint32_t gt_run = 0, eq_run = 0;                // counts over earlier chunks
-  constexpr int GS = NC >= 16 ? kGroup / 2 : kGroup;   // register budget of the widest variant
-  auto emit_group = [&](int c0, int G, const uint32_t (*kk)[4]) {
-    uint32_t packed[GS], incl[GS];
+  if constexpr (NC > 0) {
+    // Bitmaps: chunk c of thread t covers positions 4*(c*kThreads + t) + e,
+    // so the 8 lanes t = 8m..8m+7 fill word c*kThreads/8 + m, 4 bits each.
+    const int sub = lane & 7;
 #pragma unroll
-    for (int g = 0; g < GS; ++g) {
-      if (g < G) {
-        uint32_t pk = 0;
+    for (int c = 0; c < NC; ++c) {
+      uint32_t gn = 0u, en = 0u;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const uint32_t m = kk[g][e] & mask;
-          const bool valid = kk[g][e] != 0u;
-          pk += (valid && m > prefix) ? 1u : 0u;
-          pk += (valid && m == prefix) ? 0x10000u : 0u;
-        }
-        packed[g] = pk;
-        incl[g] = wave_incl_scan(pk, lane);
-        if (lane == 63) sh.wsum[g * kWaves + wave] = incl[g];
+      for (int e = 0; e < 4; ++e) {
+        const uint32_t k = keys[c][e], m = k & mask;
+        const bool valid = k != 0u;
+        gn |= (valid && m > prefix) ? (1u << e) : 0u;
+        en |= (valid && m == prefix) ? (1u << e) : 0u;
+      }
+      // OR over lanes l-7..l: complete at lanes 7 and 15 of each DPP row
+      uint32_t gw = gn << (4 * sub), ew = en << (4 * sub);
+      gw |= dpp<0x111, 0xf>(gw);
+      ew |= dpp<0x111, 0xf>(ew);
+      gw |= dpp<0x112, 0xf>(gw);
+      ew |= dpp<0x112, 0xf>(ew);
+      gw |= dpp<0x114, 0xf>(gw);
+      ew |= dpp<0x114, 0xf>(ew);
+      if (sub == 7) {
+        sh.gt_bits[c * (kThreads / 8) + (tid >> 3)] = gw;
+        sh.eq_bits[c * (kThreads / 8) + (tid >> 3)] = ew;
       }
     }
     __syncthreads();
+    // One thread per J consecutive words, in position order.
+    constexpr int W = Shared<NC, C>::kWords;
+    constexpr int J = W >= kThreads ? W / kThreads : 1;
+    const bool act = tid * J < W;
+    uint32_t gw[J], ew[J], gc = 0u, ec = 0u;
 #pragma unroll
-    for (int g = 0; g < GS; ++g) {
-      if (g < G) {
-        uint32_t before = 0, total = 0;
-#pragma unroll
-        for (int w = 0; w < kWaves; ++w) {
-          const uint32_t v = sh.wsum[g * kWaves + w];
-          before += (w < wave) ? v : 0u;
-          total += v;
-        }
-        const uint32_t excl = before + incl[g] - packed[g];
-        uint32_t g_b = gt_run + (excl & 0xffffu), e_b = eq_run + (excl >> 16);
-        const int pos0 = ((c0 + g) * kThreads + tid) * 4;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const uint32_t m = kk[g][e] & mask;
-          const bool valid = kk[g][e] != 0u;
-          const bool gt = valid && m > prefix, eq = valid && m == prefix;
-          if (gt || (eq && e_b < k_rem)) out[g_b + min(e_b, k_rem)] = pos0 + e;
-          g_b += gt ? 1u : 0u;
-          e_b += eq ? 1u : 0u;
-        }
-        gt_run += total & 0xffffu;
-        eq_run += total >> 16;
-      }
+    for (int j = 0; j < J; ++j) {
+      gw[j] = act ? sh.gt_bits[tid * J + j] : 0u;
+      ew[j] = act ? sh.eq_bits[tid * J + j] : 0u;
+      gc += __builtin_popcount(gw[j]);
+      ec += __builtin_popcount(ew[j]);
     }
-    __syncthreads();                              // wsum is reused by the next group
-  };
-  if constexpr (NC > 0) {
+    const uint32_t gi = wave_incl_scan(gc), ei = wave_incl_scan(ec);
+    if (lane == 63) {
+      sh.wsum[wave] = gi;
+      sh.wsum[kWaves + wave] = ei;
+    }
+    __syncthreads();
+    uint32_t g_b = gi - gc, e_b = ei - ec;        // counts before my first word
+    for (int w = 0; w < wave; ++w) {
+      g_b += sh.wsum[w];
+      e_b += sh.wsum[kWaves + w];
+    }
 #pragma unroll
-    for (int c0 = 0; c0 < NC; c0 += GS)
-      if (c0 < iters) emit_group(c0, min(GS, iters - c0), keys + c0);
+    for (int j = 0; j < J; ++j) {
+      // equal positions are taken while fewer than k_rem came before
+      uint32_t ek = ew[j];
+      if (e_b >= k_rem) {
+        ek = 0u;
+      } else if (e_b + __builtin_popcount(ek) > k_rem) {
+        uint32_t keep = 0u, rest = ek;
+        for (uint32_t q = k_rem - e_b; q > 0u; --q) {
+          const uint32_t low = rest & (0u - rest);
+          keep |= low;
+          rest ^= low;
+        }
+        ek = keep;
+      }
+      uint32_t sel = gw[j] | ek;
+      uint32_t slot = g_b + min(e_b, k_rem);
+      const int base = 32 * (tid * J + j);
+      while (sel != 0u) {
+        put(slot++, base + __builtin_ctz(sel));
+        sel &= sel - 1u;
+      }
+      g_b += __builtin_popcount(gw[j]);
+      e_b += __builtin_popcount(ew[j]);
+    }
+    __syncthreads();                              // the stage is complete
   } else {
-    for (int c0 = 0; c0 < iters; c0 += GS) {
-      uint32_t kk[GS][4];
-      const int G = min(GS, iters - c0);
+    // Ordered emission: chunk c holds positions 4*(c*kThreads + tid) + 0..3,
+    // so positions run over (chunk, thread, element).  A group of chunks is
+    // scanned at once (one barrier): per chunk a block-wide exclusive scan of
+    // the packed (gt, eq) counts, plus running totals over earlier chunks.
+    uint32_t gt_run = 0, eq_run = 0;              // counts over earlier chunks
+    auto emit_group = [&](int c0, int G, const uint32_t (*kk)[4]) {
+      uint32_t packed[kGroup], incl[kGroup];
 #pragma unroll
-      for (int g = 0; g < GS; ++g)
+      for (int g = 0; g < kGroup; ++g) {
+        if (g < G) {
+          uint32_t pk = 0;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const uint32_t m = kk[g][e] & mask;
+            const bool valid = kk[g][e] != 0u;
+            pk += (valid && m > prefix) ? 1u : 0u;
+            pk += (valid && m == prefix) ? 0x10000u : 0u;
+          }
+          packed[g] = pk;
+          incl[g] = wave_incl_scan(pk);
+          if (lane == 63) sh.wsum[g * kWaves + wave] = incl[g];
+        }
+      }
+      __syncthreads();
+#pragma unroll
+      for (int g = 0; g < kGroup; ++g) {
+        if (g < G) {
+          uint32_t before = 0, total = 0;
+#pragma unroll
+          for (int w = 0; w < kWaves; ++w) {
+            const uint32_t v = sh.wsum[g * kWaves + w];
+            before += (w < wave) ? v : 0u;
+            total += v;
+          }
+          const uint32_t excl = before + incl[g] - packed[g];
+          uint32_t g_b = gt_run + (excl & 0xffffu), e_b = eq_run + (excl >> 16);
+          const int pos0 = ((c0 + g) * kThreads + tid) * 4;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const uint32_t m = kk[g][e] & mask;
+            const bool valid = kk[g][e] != 0u;
+            const bool gt = valid && m > prefix, eq = valid && m == prefix;
+            if (gt || (eq && e_b < k_rem)) put(g_b + min(e_b, k_rem), pos0 + e);
+            g_b += gt ? 1u : 0u;
+            e_b += eq ? 1u : 0u;
+          }
+          gt_run += total & 0xffffu;
+          eq_run += total >> 16;
+        }
+      }
+      __syncthreads();                            // wsum is reused by the next group
+    };
+    for (int c0 = 0; c0 < iters; c0 += kGroup) {
+      uint32_t kk[kGroup][4];
+      const int G = min(kGroup, iters - c0);
+#pragma unroll
+      for (int g = 0; g < kGroup; ++g)
         if (g < G) load_keys(c0 + g, kk[g]);
       emit_group(c0, G, kk);
     }
   }
   // K' = min(K, n) = K here (n > K), so no padding is needed.
+  if (staged) {
+    if ((K & 3) == 0 && (reinterpret_cast<uintptr_t>(out) & 15u) == 0) {
+      for (int j = tid; j < K / 4; j += kThreads)
+        st16(out + 4 * j, u32x4{sh.hist[4 * j], sh.hist[4 * j + 1], sh.hist[4 * j + 2], sh.hist[4 * j + 3]});
+    } else {
+      for (int j = tid; j < K; j += kThreads) out[j] = (int32_t)sh.hist[j];
+    }
+  }
 }
 
 }  // namespace
@@ -249,14 +380,16 @@ hipError_t launch_topk(const TopkLaunch& a, hipStream_t s) {
   const int chunks = (n_max + 3) / 4;
   const int iters = (chunks + kThreads - 1) / kThreads;
   dim3 grid(rows), block(kThreads);
+  // short rows come in large numbers (prefill): small histograms keep two
+  // work-groups per CU; long rows are few and get the widest spreading
   if (iters <= 2)
-    hipLaunchKernelGGL(topk_kernel<2>, grid, block, 0, s, a);
+    hipLaunchKernelGGL((topk_kernel<2, 2>), grid, block, 0, s, a);
   else if (iters <= 8)
-    hipLaunchKernelGGL(topk_kernel<8>, grid, block, 0, s, a);
+    hipLaunchKernelGGL((topk_kernel<8, 8>), grid, block, 0, s, a);
   else if (iters <= 16)
-    hipLaunchKernelGGL(topk_kernel<16>, grid, block, 0, s, a);
+    hipLaunchKernelGGL((topk_kernel<16, 8>), grid, block, 0, s, a);
   else
-    hipLaunchKernelGGL(topk_kernel<0>, grid, block, 0, s, a);
+    hipLaunchKernelGGL((topk_kernel<0, 8>), grid, block, 0, s, a);
   return hipGetLastError();
 }
 

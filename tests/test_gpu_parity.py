@@ -115,6 +115,48 @@ def test_topk_bitexact(shape):
             assert np.array_equal(got[b, i], ref), (b, i, n)
 
 
+def _special_rows(kind, n_rows, n, seed):
+    """Rows that steer the selector into its less common branches."""
+    rng = np.random.default_rng(seed)
+    if kind == "inf":            # infinite scores: no finite value range
+        x = rng.standard_normal((n_rows, n)).astype(np.float32)
+        m = rng.random((n_rows, n))
+        x[m < 0.01] = np.inf
+        x[(m >= 0.01) & (m < 0.05)] = -np.inf
+    elif kind == "outliers":     # a few huge values squeeze the rest into few value bins
+        x = rng.standard_normal((n_rows, n)).astype(np.float32)
+        x[:, rng.integers(0, n, 20)] *= 1e6
+    elif kind == "narrow":       # neighbouring floats, many exact ties
+        x = (1.0 + rng.integers(0, 3000, (n_rows, n)) * 2.0 ** -23).astype(np.float32)
+    elif kind == "equal":
+        x = np.full((n_rows, n), 3.5, dtype=np.float32)
+    elif kind == "two_values":
+        x = np.where(rng.random((n_rows, n)) < 0.5, 1.0, 2.0).astype(np.float32)
+    elif kind == "subnormal":    # value range too small to scale into bins
+        x = (rng.integers(-50, 50, (n_rows, n)) * 1.4e-45).astype(np.float32)
+    elif kind == "huge_range":   # max - min overflows fp32
+        x = rng.standard_normal((n_rows, n)).astype(np.float32)
+        x[:, 0], x[:, 1] = 3.0e38, -3.0e38
+    else:
+        raise ValueError(kind)
+    return torch.from_numpy(x).to(DEV)
+
+
+@pytest.mark.parametrize("kind", ["inf", "outliers", "narrow", "equal", "two_values", "subnormal", "huge_range"])
+@pytest.mark.parametrize("Lk,K", [(6000, 2048), (30000, 2048), (50000, 100), (80000, 2048), (20000, 5000)])
+def test_topk_special_rows(kind, Lk, K):
+    dsa = _dsa()
+    B, Lq = 1, 2
+    scores = _special_rows(kind, B * Lq, Lk, seed=Lk + K).view(B, Lq, Lk).contiguous()
+    cfg = C.scaled(C.DECODE_32K, batch=B, q_len=Lq, kv_len=Lk, topk=K)
+    idx = dsa.topk(dsa.make_problem(cfg), scores)
+    torch.cuda.synchronize()
+    got, host = idx.cpu().numpy(), scores.cpu().numpy()
+    for i in range(Lq):
+        ref = O.topk_row(host[0, i], O.visible_count(Lq, Lk, i), K)
+        assert np.array_equal(got[0, i], ref), (kind, i)
+
+
 def _oracle_sets(cfg, host):
     qf, kf = O.as_f64_index_inputs(host["q_idx"], host["q_scale"], host["k_idx"], host["k_scale"])
     sc = O.index_scores(qf, kf, host["head_w"], cfg.q_len, cfg.kv_len)
