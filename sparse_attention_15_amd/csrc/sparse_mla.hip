@@ -11,21 +11,25 @@
 // "DeepSeek-V3.2-Exp" token-ids page (n_heads 128, kv_lora_rank 512,
 // qk_rope_head_dim 64).
 //
-// bf16 kernel, one work-group per (query, key split), 8 waves in 4 pairs:
+// bf16 kernel, one work-group per (query, key split), 4 waves of 32 heads:
 //  - the selected rows are gathered from HBM in blocks of 32 straight into
 //    LDS (global_load_lds: each lane moves one 16-byte chunk of a 1152-byte
-//    row, no registers involved), three blocks in flight, and staged once
-//    for all 128 heads;
-//  - S^T = KV_blk . Q^T on 32x32x16 MFMA, the 576 dims split between the two
-//    waves of a pair and the partial tiles summed through LDS (Q stays in
-//    registers); each lane owns one head, so the softmax max/sum are
-//    lane-local plus one cross-half exchange;
-//  - online softmax in base 2, with the running max only raised when a block
-//    exceeds it by more than 2^8 (the accumulator rescale is then rare);
+//    row, no registers involved), three stage buffers with two blocks in
+//    flight, and staged once for all 128 heads; the next-but-one block's
+//    gather is issued from inside the current block's QK steps;
+//  - S^T = KV_blk . Q^T on 32x32x16 MFMA over all 576 dims, Q in registers
+//    (each wave's 32 head rows staged once through LDS); each lane owns one
+//    head, so the softmax max/sum are lane-local plus one cross-half
+//    exchange;
+//  - online softmax in base 2 with the logit scale folded into the exponent's
+//    FMA, the running max only raised when a block exceeds it by more than
+//    2^8 (the accumulator rescale is then rare);
 //  - O^T += V^T . P^T on MFMA with P taken straight from the S^T registers
 //    and the value operand read transposed from the row-major tile
 //    (ds_read_b64_tr_b16), so no second copy of the values is staged; the
-//    two partners cover the two halves of the 512 value dims.
+//    second key half's P is formed while the first half's PV MFMAs run;
+//  - output rows leave through the idle stage buffers, 1 KB contiguous per
+//    store instruction.
 // Decode-shaped launches split each query's list over several work-groups
 // and merge the partial (O, lse) pairs in a second kernel.
 #include "dsa_device.h"
