@@ -281,6 +281,10 @@ def main():
     ap.add_argument("--with-producer", action="store_true",
                     help="FP8-index workloads: start each step from bf16 index activations and run the FP8 "
                          "producer (Hadamard rotation + ue8m0/E4M3 quantisation) before the fused path")
+    ap.add_argument("--with-projections", action="store_true",
+                    help="bf16-index workloads: each step first projects the index queries from a query latent "
+                         "and the head weights from a hidden state, and un-absorbs the attention output after "
+                         "(bf16 GEMMs on synthetic weights)")
     ap.add_argument("--decode-loop", action="store_true",
                     help="decode workloads: each step appends one token per sequence to caches with room for "
                          "them and runs the fused path for one query at the grown context; the `steps` "
@@ -325,6 +329,20 @@ def main():
             st_["k_scale"] = torch.empty(st_["k_idx"].shape[:-1], dtype=torch.uint8, device=dev)
     else:
         sets = [generate(cfg, device=dev, set_index=s) for s in range(nsets)]
+    projections = args.with_projections
+    if projections:
+        if cfg.index_dtype != "bf16" or producer or p.out_dtype != dsa.DSA_BF16:
+            print("--with-projections applies to bf16-index workloads with bf16 output", file=sys.stderr)
+            sys.exit(2)
+        from dsa_workloads import generate_projection_inputs
+        from dsa_workloads.generate import V_HEAD_DIM
+        for si, st_ in enumerate(sets):
+            st_.update(generate_projection_inputs(cfg, device=dev, set_index=si))
+            st_["q_proj"] = torch.empty_like(st_["q_idx"])
+            st_["w_out"] = torch.empty_like(st_["head_w"])
+            st_["o_final"] = torch.empty(cfg.batch, cfg.q_len, cfg.attn_heads, V_HEAD_DIM, dtype=torch.bfloat16,
+                                         device=dev)
+    proj_ev = []
     ws = torch.empty(dsa.workspace_size(p, dsa.DSA_OP_FORWARD), dtype=torch.uint8, device=dev)
     odt = torch.float32 if p.out_dtype == dsa.DSA_F32 else torch.bfloat16
     outs = [torch.empty(cfg.batch, cfg.q_len, cfg.attn_heads, cfg.v_dim, dtype=odt, device=dev) for _ in sets]
@@ -347,14 +365,33 @@ def main():
                 e1.record()
                 prod_ev.append((e0, e1))
             q_idx, k_idx = s["q_codes"], s["k_codes"]
+        head_w = s["head_w"]
+        if projections:
+            if events is not None:
+                pe = [torch.cuda.Event(enable_timing=True) for _ in range(5)]
+                pe[0].record()
+            dsa.index_q_proj(p, s["cq"], s["wq_b"], out=s["q_proj"])
+            if events is not None:
+                pe[1].record()
+            dsa.head_weights_proj(p, s["x"], s["w_proj"], out=s["w_out"])
+            if events is not None:
+                pe[2].record()
+            q_idx, head_w = s["q_proj"], s["w_out"]
         ev = None
         if events is not None:
             import ctypes
             ev = ctypes.cast(ctypes.byref(events.arr, ctypes.sizeof(ctypes.c_void_p) * 2 * base),
                              ctypes.POINTER(ctypes.c_void_p))
-        dsa.forward(p, q_idx, s["q_scale"], k_idx, s["k_scale"], s["head_w"], s["q_attn"], s["kv"],
+        dsa.forward(p, q_idx, s["q_scale"], k_idx, s["k_scale"], head_w, s["q_attn"], s["kv"],
                     out=outs[k % nsets], lse=lses[k % nsets], workspace=ws, events=ev,
                     n_events=2 * slots_per_step)
+        if projections:
+            if events is not None:
+                pe[3].record()
+            dsa.out_unabsorb(p, outs[k % nsets], s["w_uv"], out=s["o_final"])
+            if events is not None:
+                pe[4].record()
+                proj_ev.append(pe)
 
     for k in range(args.warmup):
         step(k)
@@ -411,6 +448,33 @@ def main():
                     algorithmic_bytes=pbytes, achieved=round(gbs, 1), unit="GB/s", peak=HBM_PEAK_GBS,
                     frac=round(gbs / HBM_PEAK_GBS, 4),
                     note="q rows (B*Lq*H) and key rows (B*Lk): 128 bf16 in, 128 E4M3 codes + 1 scale byte out")
+    proj = None
+    if projections:
+        M = cfg.batch * cfg.q_len
+        s0 = sets[0]
+        R, hid = s0["cq"].shape[-1], s0["x"].shape[-1]
+        HD, H, NH, Dv, V = cfg.index_heads * cfg.index_dim, cfg.index_heads, cfg.attn_heads, cfg.v_dim, V_HEAD_DIM
+        work = {  # (algorithmic bytes, flops) per call: operands read once, output written once
+            "index_q": (2 * (M * R + HD * R + M * HD), 2 * M * HD * R),
+            "head_weights": (2 * (M * hid + H * hid) + 4 * M * H, 2 * M * H * hid),
+            "unabsorb": (2 * (M * NH * Dv + NH * V * Dv + M * NH * V), 2 * M * NH * V * Dv),
+        }
+        slots = {"index_q": (0, 1), "head_weights": (1, 2), "unabsorb": (3, 4)}
+        kern = "gemm_skinny_kernel" if M <= 32 else "gemm_tile_kernel"
+        proj = {"kernel": kern, "bound": "hbm" if M <= 32 else "mfma"}
+        for name, (a_, b_) in slots.items():
+            ms_ = sum(e[a_].elapsed_time(e[b_]) for e in proj_ev) / max(1, len(proj_ev))
+            nbytes, flops = work[name]
+            if M <= 32:
+                ach = nbytes / (ms_ * 1e-3) / 1e9
+                proj[name] = dict(ms=round(ms_, 5), algorithmic_bytes=nbytes, achieved=round(ach, 1), unit="GB/s",
+                                  peak=HBM_PEAK_GBS, frac=round(ach / HBM_PEAK_GBS, 4))
+            else:
+                ach = flops / (ms_ * 1e-3) / 1e12
+                proj[name] = dict(ms=round(ms_, 5), flops=flops, achieved=round(ach, 1), unit="TFLOP/s",
+                                  peak=MFMA_BF16_PEAK_TFLOPS, frac=round(ach / MFMA_BF16_PEAK_TFLOPS, 4))
+        proj["note"] = ("inside every step: index queries from a [T,%d] latent, head weights from a [T,%d] hidden "
+                        "state, per-head un-absorption to v_head_dim %d; events around each call" % (R, hid, V))
     res = {
         "metric": "DSA queries/sec (indexer+top-k+sparse MLA)",
         "value": round(qps, 1),
@@ -424,7 +488,7 @@ def main():
         "vs_baseline": None,
         "dtype": {"bf16": "bf16", "f32": "f32", "fp8_e4m3": "fp8_e4m3+bf16"}[cfg.index_dtype],
         "data": "synthetic (seeded generators; no dataset or weights)",
-        "config": {"workload": cfg.name + ("+fp8_producer" if producer else ""), "batch": cfg.batch, "q_len": cfg.q_len, "kv_len": cfg.kv_len,
+        "config": {"workload": cfg.name + ("+fp8_producer" if producer else "") + ("+projections" if projections else ""), "batch": cfg.batch, "q_len": cfg.q_len, "kv_len": cfg.kv_len,
                    "index_heads": cfg.index_heads, "index_dim": cfg.index_dim, "topk": cfg.topk,
                    "attn_heads": cfg.attn_heads, "qk_dim": cfg.qk_dim, "v_dim": cfg.v_dim,
                    "query_chunks": n_chunks, "attn_splits": splits, "input_sets": nsets},
@@ -432,6 +496,7 @@ def main():
         "stage_ms": {name: round(v, 5) for name, v in zip(dsa.STAGE_NAMES, stage_ms)},
         "ms_per_step_evented": round(evented_ms, 5),
         **({"producer": prod} if prod else {}),
+        **({"projections": proj} if proj else {}),
         "path_hbm_frac": round(path_bytes / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
         "path_algorithmic_bytes": path_bytes,
         "path_mfma_frac_bf16": round((al["index_flops"] + al["attn_flops"]) / (ms_per_step * 1e-3) / 1e12

@@ -193,3 +193,32 @@ def random_score_rows(n_rows: int, row_len: int, seed: int, device="cpu",
         x = torch.where(r < 0.05, torch.zeros_like(x), x)
         x = torch.where((r >= 0.05) & (r < 0.10), torch.full_like(x, -0.0), x)
     return x.contiguous()
+
+
+# Sizes of the projections in the released configuration excerpt.
+Q_LORA_RANK, HIDDEN, V_HEAD_DIM = 1536, 7168, 128
+
+
+def generate_projection_inputs(cfg: DSAConfig, device="cpu", set_index: int = 0, q_lora_rank: int = Q_LORA_RANK,
+                               hidden: int = HIDDEN, v_head_dim: int = V_HEAD_DIM) -> dict:
+    """Seeded bf16 inputs of the projections on either side of the path.
+
+      cq     [B,Lq,R]        ~ N(0,1)      query latent
+      wq_b   [H*D, R]        ~ N(0, 1/R)   (index queries come out ~ N(0,1))
+      x      [B,Lq,hidden]   ~ N(0,1)      hidden state
+      w_proj [H, hidden]     ~ N(0, 1/(hidden*H))   (head weights ~ N(0, 1/H))
+      o_lat  [B,Lq,NH,Dv]    ~ N(0,1)      latent attention output
+      w_uv   [NH, V, Dv]     ~ N(0, 1/Dv)
+    """
+    B, Lq, H, D = cfg.batch, cfg.q_len, cfg.index_heads, cfg.index_dim
+    NH, Dv = cfg.attn_heads, cfg.v_dim
+    s = (cfg.seed, set_index, "proj")
+    bf = torch.bfloat16
+    return dict(
+        cq=_normal_stored((B, Lq, q_lora_rank), _seed(*s, "cq"), device, bf),
+        wq_b=_normal((H * D, q_lora_rank), _seed(*s, "wq_b"), device, std=1.0 / math.sqrt(q_lora_rank)).to(bf),
+        x=_normal_stored((B, Lq, hidden), _seed(*s, "x"), device, bf),
+        w_proj=_normal((H, hidden), _seed(*s, "w_proj"), device, std=1.0 / math.sqrt(hidden * H)).to(bf),
+        o_lat=_normal_stored((B, Lq, NH, Dv), _seed(*s, "o_lat"), device, bf),
+        w_uv=_normal((NH, v_head_dim, Dv), _seed(*s, "w_uv"), device, std=1.0 / math.sqrt(Dv)).to(bf),
+    )

@@ -218,6 +218,47 @@ dsa_status_t dsa_cache_append(const dsa_problem_t* prob, int32_t n_new,
 dsa_status_t dsa_index_rotate_quantize(const void* x, dsa_dtype_t x_dtype, int64_t rows, int32_t dim,
                                        uint8_t* codes, uint8_t* scales, hipStream_t stream);
 
+/* Projections on either side of the path (bf16 MFMA GEMMs, fp32 accumulation).
+ * All operands bf16, row-major, 16-byte aligned; inner sizes multiples of 8.
+ * Tokens are the B * Lq rows of the problem.
+ *
+ * Index query from the query latent (HF doc "DeepSeek-V3.2", usage notes:
+ * the indexer scores queries from the low-rank query latent through its
+ * wq_b projection, sized by q_lora_rank; q_lora_rank 1536, index_n_heads 64,
+ * index_head_dim 128 in the released configuration excerpt, atlas token-ids
+ * page):
+ *   cq     [B][Lq][q_lora_rank]
+ *   wq_b   [H*D][q_lora_rank]       output row h*D + d is head h, dim d
+ *   q_idx  [B][Lq][H][D]            q_dtype: DSA_BF16 or DSA_F32
+ *   q_idx[t][h][d] = sum_r cq[t][r] * wq_b[h*D + d][r].
+ * For the FP8 index path, produce bf16 here and pass it to
+ * dsa_index_rotate_quantize.
+ */
+dsa_status_t dsa_index_q_proj(const dsa_problem_t* prob, int32_t q_lora_rank, const void* cq, const void* wq_b,
+                              void* q_idx, dsa_dtype_t q_dtype, hipStream_t stream);
+
+/* Per-query head weights from the hidden state (the indexer's weights_proj,
+ * kept out of FP8 in the usage example of the same doc; dim 7168 in the
+ * configuration):
+ *   x       [B][Lq][dim]
+ *   w_proj  [H][dim]
+ *   head_w  [B][Lq][H] fp32:  head_w[t][h] = sum_i x[t][i] * w_proj[h][i]
+ * (no bias, no extra constant).
+ */
+dsa_status_t dsa_head_weights_proj(const dsa_problem_t* prob, int32_t dim, const void* x, const void* w_proj,
+                                   float* head_w, hipStream_t stream);
+
+/* Un-absorption of the attention output: the value half of MLA's key/value
+ * up-projection applied per head to the latent output (kv_lora_rank 512 and
+ * v_head_dim 128 in the configuration):
+ *   o_latent [B][Lq][NH][Dv]          dsa_sparse_mla_attn / dsa_forward output (bf16)
+ *   w_uv     [NH][v_head_dim][Dv]
+ *   out      [B][Lq][NH][v_head_dim]  out_dtype: DSA_BF16 or DSA_F32
+ *   out[t][a][v] = sum_c o_latent[t][a][c] * w_uv[a][v][c].
+ */
+dsa_status_t dsa_out_unabsorb(const dsa_problem_t* prob, int32_t v_head_dim, const void* o_latent, const void* w_uv,
+                              void* out, dsa_dtype_t out_dtype, hipStream_t stream);
+
 #define DSA_OP_ATTN 1
 #define DSA_OP_FORWARD 2
 /* Workspace bytes needed by dsa_sparse_mla_attn (op = DSA_OP_ATTN) or

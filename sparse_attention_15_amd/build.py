@@ -21,7 +21,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(HERE, "_build")
 LIB_PATH = os.path.join(HERE, "libdsa.so")
 
-SOURCES = ["indexer.hip", "topk.hip", "sparse_mla.hip", "fp8_producer.hip", "kv_cache.hip", "dsa_api.cpp"]
+SOURCES = ["indexer.hip", "topk.hip", "sparse_mla.hip", "fp8_producer.hip", "kv_cache.hip", "gemm.hip", "dsa_api.cpp"]
 
 ARCH = "gfx950"
 COMMON_FLAGS = [

@@ -210,6 +210,24 @@ dsa_status_t forward_impl(const dsa_problem_t* prob, const void* q_idx, const ui
   return DSA_OK;
 }
 
+// Shared checks of the projections: bf16 operands with 16-byte rows.
+dsa_status_t run_gemm(const void* a, const void* b, void* c, int m, int n, int k, int batch, int64_t lda,
+                      int64_t ldb, int64_t ldc, int64_t sa, int64_t sb, int64_t sc, dsa_dtype_t c_dtype,
+                      hipStream_t stream) {
+  if (!a || !b || !c || k < 8 || (k & 7) || (lda & 7) || (ldb & 7)) return DSA_ERR_INVALID_ARGUMENT;
+  if (c_dtype != DSA_BF16 && c_dtype != DSA_F32) return DSA_ERR_INVALID_ARGUMENT;
+  if (!aligned16(a) || !aligned16(b) || (reinterpret_cast<uintptr_t>(c) & 3u)) return DSA_ERR_INVALID_ARGUMENT;
+  GemmLaunch g;
+  g.A = static_cast<const uint16_t*>(a);
+  g.B = static_cast<const uint16_t*>(b);
+  g.C = c;
+  g.M = m; g.N = n; g.K = k; g.batch = batch;
+  g.lda = lda; g.ldb = ldb; g.ldc = ldc;
+  g.sa = sa; g.sb = sb; g.sc = sc;
+  g.c_f32 = c_dtype == DSA_F32;
+  return hip_status(launch_gemm_bt(g, stream));
+}
+
 }  // namespace
 
 extern "C" {
@@ -329,6 +347,40 @@ dsa_status_t dsa_index_rotate_quantize(const void* x, dsa_dtype_t x_dtype, int64
   if (!x || !codes || !scales || !aligned16(x) || (reinterpret_cast<uintptr_t>(codes) & 7u))
     return DSA_ERR_INVALID_ARGUMENT;
   return hip_status(launch_rotate_quant(x, x_dtype == DSA_F32, rows, codes, scales, stream));
+}
+
+dsa_status_t dsa_index_q_proj(const dsa_problem_t* prob, int32_t q_lora_rank, const void* cq, const void* wq_b,
+                              void* q_idx, dsa_dtype_t q_dtype, hipStream_t stream) {
+  Path path;
+  const dsa_status_t st = check_problem(prob, &path);
+  if (st != DSA_OK) return st;
+  const dsa_problem_t& p = *prob;
+  const int hd = p.index_heads * p.index_dim;
+  return run_gemm(cq, wq_b, q_idx, p.batch * p.q_len, hd, q_lora_rank, 1, q_lora_rank, q_lora_rank, hd, 0, 0, 0,
+                  q_dtype, stream);
+}
+
+dsa_status_t dsa_head_weights_proj(const dsa_problem_t* prob, int32_t dim, const void* x, const void* w_proj,
+                                   float* head_w, hipStream_t stream) {
+  Path path;
+  const dsa_status_t st = check_problem(prob, &path);
+  if (st != DSA_OK) return st;
+  const dsa_problem_t& p = *prob;
+  return run_gemm(x, w_proj, head_w, p.batch * p.q_len, p.index_heads, dim, 1, dim, dim, p.index_heads, 0, 0, 0,
+                  DSA_F32, stream);
+}
+
+dsa_status_t dsa_out_unabsorb(const dsa_problem_t* prob, int32_t v_head_dim, const void* o_latent, const void* w_uv,
+                              void* out, dsa_dtype_t out_dtype, hipStream_t stream) {
+  Path path;
+  const dsa_status_t st = check_problem(prob, &path);
+  if (st != DSA_OK) return st;
+  const dsa_problem_t& p = *prob;
+  if (v_head_dim < 1) return DSA_ERR_INVALID_ARGUMENT;
+  const int NH = p.attn_heads, Dv = p.v_dim;
+  // batch z = head: A rows are tokens with stride NH * Dv, offset z * Dv
+  return run_gemm(o_latent, w_uv, out, p.batch * p.q_len, v_head_dim, Dv, NH, (int64_t)NH * Dv, Dv,
+                  (int64_t)NH * v_head_dim, Dv, (int64_t)v_head_dim * Dv, v_head_dim, out_dtype, stream);
 }
 
 int32_t dsa_forward_attn_splits(const dsa_problem_t* prob) {

@@ -75,6 +75,19 @@ hipError_t launch_attn_f32(const AttnLaunch& a, hipStream_t s);
 hipError_t launch_attn_bf16(const AttnLaunch& a, hipStream_t s);
 hipError_t launch_attn_combine(const AttnLaunch& a, hipStream_t s);
 
+// C[m][n] = sum_k A[m][k] * B[n][k], bf16 in, fp32 accumulate; batch z adds
+// z * s{a,b,c} elements to the bases.  K % 8 == 0, rows 16-byte aligned.
+struct GemmLaunch {
+  const uint16_t* A;
+  const uint16_t* B;
+  void* C;
+  int M, N, K, batch;
+  int64_t lda, ldb, ldc;   // row strides (elements)
+  int64_t sa, sb, sc;      // batch strides (elements)
+  int c_f32;               // 1: fp32 output, 0: bf16
+};
+hipError_t launch_gemm_bt(const GemmLaunch& g, hipStream_t s);
+
 // Split count the bf16 attention uses for a launch of `rows` queries.
 int attn_splits_bf16(int rows, int K);
 

@@ -1,0 +1,211 @@
+// Projections on either side of the DSA path as bf16 MFMA GEMMs on gfx950.
+//
+//   C[m][n] = sum_k A[m][k] * B[n][k]      (both operands k-contiguous)
+//
+// batched with strides, bf16 inputs, fp32 accumulation, bf16 or fp32 output.
+// The three projections (HF model doc "DeepSeek-V3.2": the indexer's wq_b on
+// the query latent, its weights_proj kept out of FP8; sizes from the released
+// configuration excerpt on the atlas "DeepSeek-V3.2-Exp" token-ids page):
+//   index query:   A = query latent [T][q_lora_rank], B = wq_b [H*D][q_lora_rank]
+//   head weights:  A = hidden state [T][dim],         B = weights_proj [H][dim]
+//   un-absorption: per head a, A = O[:, a, :] [T][kv_lora_rank] (row stride
+//                  NH * kv_lora_rank), B = W_UV[a] [v_head_dim][kv_lora_rank]
+//
+// Tile kernel (more than 32 rows): 4 waves as 2 x 2, each a TM x TN block of
+// 32x32x16 MFMAs; 64-k stages (128 bytes per row) in LDS with chunk c of row r
+// stored at c ^ (r & 7), so the 32 rows of an operand read spread over the
+// banks; the next stage is loaded into registers while the current one is
+// multiplied, one barrier per stage.
+// Skinny kernel (at most 32 rows, the decode shapes, which stream the
+// weights): one 32 x 32 output tile per work-group; its 4 waves take
+// interleaved 64-k stages through private LDS buffers (no barriers in the
+// loop) and add their accumulators through LDS at the end, so four times as
+// many weight loads are in flight per output tile.
+#include "dsa_device.h"
+#include "dsa_internal.h"
+
+namespace dsa {
+namespace {
+
+constexpr int kGK = 64;                          // k per stage: 8 chunks of 16 bytes per row
+
+__device__ __forceinline__ uint32_t tile_off(int r, int c) { return (uint32_t)(r * 128 + ((c ^ (r & 7)) << 4)); }
+
+__device__ __forceinline__ void store_c(const GemmLaunch& g, void* cb, int m, int n, float v) {
+  if (g.c_f32)
+    static_cast<float*>(cb)[(int64_t)m * g.ldc + n] = v;
+  else
+    static_cast<uint16_t*>(cb)[(int64_t)m * g.ldc + n] = f32_to_bf16_bits(v);
+}
+
+template <int TM, int TN>
+__global__ __launch_bounds__(256) void gemm_tile_kernel(GemmLaunch g) {
+  constexpr int BM = 2 * TM, BN = 2 * TN, IM = TM / 32, IN = TN / 32;
+  constexpr int APT = BM * 8 / 256, BPT = BN * 8 / 256;   // 16-byte chunks per thread and stage
+  __shared__ __attribute__((aligned(16))) uint8_t lds[2][(BM + BN) * 128];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int n0 = blockIdx.x * BN, m0 = blockIdx.y * BM;
+  const uint16_t* A = g.A + (int64_t)blockIdx.z * g.sa;
+  const uint16_t* B = g.B + (int64_t)blockIdx.z * g.sb;
+  const int nk = (g.K + kGK - 1) / kGK;
+
+  u32x4 ra[APT], rb[BPT];
+  auto load = [&](int kt) {
+    const int k0 = kt * kGK;
+#pragma unroll
+    for (int p = 0; p < APT; ++p) {
+      const int f = p * 256 + tid, r = f >> 3, k = k0 + 8 * (f & 7);
+      const int row = min(m0 + r, g.M - 1);
+      ra[p] = k < g.K ? ld16(A + (int64_t)row * g.lda + k) : u32x4{0u, 0u, 0u, 0u};
+    }
+#pragma unroll
+    for (int p = 0; p < BPT; ++p) {
+      const int f = p * 256 + tid, r = f >> 3, k = k0 + 8 * (f & 7);
+      const int row = min(n0 + r, g.N - 1);
+      rb[p] = k < g.K ? ld16(B + (int64_t)row * g.ldb + k) : u32x4{0u, 0u, 0u, 0u};
+    }
+  };
+  auto store = [&](int buf) {
+#pragma unroll
+    for (int p = 0; p < APT; ++p) {
+      const int f = p * 256 + tid;
+      st16(&lds[buf][tile_off(f >> 3, f & 7)], ra[p]);
+    }
+#pragma unroll
+    for (int p = 0; p < BPT; ++p) {
+      const int f = p * 256 + tid;
+      st16(&lds[buf][BM * 128 + tile_off(f >> 3, f & 7)], rb[p]);
+    }
+  };
+
+  f32x16 acc[IM][IN];
+#pragma unroll
+  for (int i = 0; i < IM; ++i)
+#pragma unroll
+    for (int j = 0; j < IN; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
+
+  load(0);
+  store(0);
+  __syncthreads();
+  const int half = lane >> 5, r32 = lane & 31;
+  for (int kt = 0; kt < nk; ++kt) {
+    const int buf = kt & 1;
+    if (kt + 1 < nk) load(kt + 1);
+    const uint8_t* base = lds[buf];
+#pragma unroll
+    for (int s = 0; s < kGK / 16; ++s) {
+      const int kc = 2 * s + half;               // this lane's 8 k-values: chunk kc
+      u32x4 av[IM], bv[IN];
+#pragma unroll
+      for (int i = 0; i < IM; ++i) av[i] = ld16(base + tile_off(wm * TM + 32 * i + r32, kc));
+#pragma unroll
+      for (int j = 0; j < IN; ++j) bv[j] = ld16(base + BM * 128 + tile_off(wn * TN + 32 * j + r32, kc));
+#pragma unroll
+      for (int i = 0; i < IM; ++i)
+#pragma unroll
+        for (int j = 0; j < IN; ++j) acc[i][j] = mfma32(av[i], bv[j], acc[i][j]);
+    }
+    if (kt + 1 < nk) store(buf ^ 1);             // buf ^ 1 was last read before the previous barrier
+    __syncthreads();
+  }
+
+  void* cb = g.c_f32 ? (void*)(static_cast<float*>(g.C) + (int64_t)blockIdx.z * g.sc)
+                     : (void*)(static_cast<uint16_t*>(g.C) + (int64_t)blockIdx.z * g.sc);
+#pragma unroll
+  for (int i = 0; i < IM; ++i)
+#pragma unroll
+    for (int j = 0; j < IN; ++j) {
+      const int n = n0 + wn * TN + 32 * j + r32;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int m = m0 + wm * TM + 32 * i + 8 * (e >> 2) + 4 * half + (e & 3);
+        if (m < g.M && n < g.N) store_c(g, cb, m, n, acc[i][j][e]);
+      }
+    }
+}
+
+__global__ __launch_bounds__(256) void gemm_skinny_kernel(GemmLaunch g) {
+  // per wave: one stage of A (32 rows) and B (32 rows), 128 bytes per row
+  __shared__ __attribute__((aligned(16))) uint8_t lds[4][64 * 128];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int n0 = blockIdx.x * 32;
+  const uint16_t* A = g.A + (int64_t)blockIdx.z * g.sa;
+  const uint16_t* B = g.B + (int64_t)blockIdx.z * g.sb;
+  const int nk = (g.K + kGK - 1) / kGK;
+  uint8_t* mine = lds[wave];
+
+  u32x4 ra[4], rb[4];
+  auto load = [&](int kt) {
+    const int k0 = kt * kGK;
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      const int f = p * 64 + lane, r = f >> 3, k = k0 + 8 * (f & 7);
+      const bool in = k < g.K;
+      ra[p] = in ? ld16(A + (int64_t)min(r, g.M - 1) * g.lda + k) : u32x4{0u, 0u, 0u, 0u};
+      rb[p] = in ? ld16(B + (int64_t)min(n0 + r, g.N - 1) * g.ldb + k) : u32x4{0u, 0u, 0u, 0u};
+    }
+  };
+  f32x16 acc;
+#pragma unroll
+  for (int e = 0; e < 16; ++e) acc[e] = 0.f;
+  const int half = lane >> 5, r32 = lane & 31;
+  int kt = wave;
+  if (kt < nk) load(kt);
+  for (; kt < nk; kt += 4) {
+    // the previous stage's operand reads were issued before these writes, and
+    // one wave's LDS operations complete in order
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      const int f = p * 64 + lane;
+      st16(mine + tile_off(f >> 3, f & 7), ra[p]);
+      st16(mine + 32 * 128 + tile_off(f >> 3, f & 7), rb[p]);
+    }
+    if (kt + 4 < nk) load(kt + 4);
+#pragma unroll
+    for (int s = 0; s < kGK / 16; ++s) {
+      const int kc = 2 * s + half;
+      const u32x4 av = ld16(mine + tile_off(r32, kc));
+      const u32x4 bv = ld16(mine + 32 * 128 + tile_off(r32, kc));
+      acc = mfma32(av, bv, acc);
+    }
+  }
+  // sum the four waves' partial tiles: waves 1..3 through LDS
+  __syncthreads();                                // every wave is done with its stage buffer
+  float* red = reinterpret_cast<float*>(&lds[0][0]);   // [3][16][64]
+  if (wave > 0)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) red[((wave - 1) * 16 + e) * 64 + lane] = acc[e];
+  __syncthreads();
+  if (wave == 0) {
+    void* cb = g.c_f32 ? (void*)(static_cast<float*>(g.C) + (int64_t)blockIdx.z * g.sc)
+                       : (void*)(static_cast<uint16_t*>(g.C) + (int64_t)blockIdx.z * g.sc);
+    const int n = n0 + r32;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const float v = acc[e] + red[e * 64 + lane] + red[(16 + e) * 64 + lane] + red[(32 + e) * 64 + lane];
+      const int m = 8 * (e >> 2) + 4 * half + (e & 3);
+      if (m < g.M && n < g.N) store_c(g, cb, m, n, v);
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_gemm_bt(const GemmLaunch& g, hipStream_t s) {
+  if (g.M <= 32) {
+    dim3 grid((g.N + 31) / 32, 1, g.batch);
+    hipLaunchKernelGGL(gemm_skinny_kernel, grid, dim3(256), 0, s, g);
+  } else if (g.M >= 128 && g.N >= 128) {
+    dim3 grid((g.N + 127) / 128, (g.M + 127) / 128, g.batch);
+    hipLaunchKernelGGL((gemm_tile_kernel<64, 64>), grid, dim3(256), 0, s, g);
+  } else {
+    dim3 grid((g.N + 63) / 64, (g.M + 63) / 64, g.batch);
+    hipLaunchKernelGGL((gemm_tile_kernel<32, 32>), grid, dim3(256), 0, s, g);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace dsa

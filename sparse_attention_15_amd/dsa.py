@@ -79,6 +79,12 @@ def lib() -> ctypes.CDLL:
     L.dsa_index_rotate_quantize.restype = ctypes.c_int
     L.dsa_cache_append.argtypes = [P, ctypes.c_int32] + [ctypes.c_void_p] * 6 + [ctypes.c_void_p]
     L.dsa_cache_append.restype = ctypes.c_int
+    for name, extra in (("dsa_index_q_proj", [I32, V, V, V, ctypes.c_int, V]),
+                        ("dsa_head_weights_proj", [I32, V, V, V, V]),
+                        ("dsa_out_unabsorb", [I32, V, V, V, ctypes.c_int, V])):
+        f = getattr(L, name)
+        f.argtypes = [P] + extra
+        f.restype = ctypes.c_int
     L.dsa_status_string.argtypes = [ctypes.c_int]
     L.dsa_status_string.restype = ctypes.c_char_p
     L.dsa_abi_version.argtypes = []
@@ -238,6 +244,55 @@ def index_rotate_quantize(x: torch.Tensor, codes: torch.Tensor = None, scales: t
                                            ctypes.c_void_p(codes.data_ptr()), ctypes.c_void_p(scales.data_ptr()),
                                            _stream()), "dsa_index_rotate_quantize")
     return codes, scales
+
+
+def _proj_out_dtype(dtype) -> int:
+    if dtype == torch.bfloat16:
+        return DSA_BF16
+    if dtype == torch.float32:
+        return DSA_F32
+    raise DSAError(DSA_ERR_INVALID_ARGUMENT, "projection outputs are bf16 or f32")
+
+
+def index_q_proj(p: Problem, cq, wq_b, out=None, dtype=torch.bfloat16) -> torch.Tensor:
+    """Index query from the query latent: cq [B, Lq, R] bf16, wq_b [H*D, R] bf16
+    -> q_idx [B, Lq, H, D]; see dsa_index_q_proj."""
+    R = cq.shape[-1]
+    if out is None:
+        out = torch.empty(p.batch, p.q_len, p.index_heads, p.index_dim, dtype=dtype, device=cq.device)
+    args = (_ptr(cq, "cq", torch.bfloat16, (p.batch, p.q_len, R)),
+            _ptr(wq_b, "wq_b", torch.bfloat16, (p.index_heads * p.index_dim, R)),
+            _ptr(out, "q_idx", out.dtype, (p.batch, p.q_len, p.index_heads, p.index_dim)))
+    _check(lib().dsa_index_q_proj(ctypes.byref(p), R, *args, _proj_out_dtype(out.dtype), _stream()),
+           "dsa_index_q_proj")
+    return out
+
+
+def head_weights_proj(p: Problem, x, w_proj, out=None) -> torch.Tensor:
+    """Head weights from the hidden state: x [B, Lq, dim] bf16, w_proj [H, dim]
+    bf16 -> head_w [B, Lq, H] fp32; see dsa_head_weights_proj."""
+    dim = x.shape[-1]
+    if out is None:
+        out = torch.empty(p.batch, p.q_len, p.index_heads, dtype=torch.float32, device=x.device)
+    args = (_ptr(x, "x", torch.bfloat16, (p.batch, p.q_len, dim)),
+            _ptr(w_proj, "w_proj", torch.bfloat16, (p.index_heads, dim)),
+            _ptr(out, "head_w", torch.float32, (p.batch, p.q_len, p.index_heads)))
+    _check(lib().dsa_head_weights_proj(ctypes.byref(p), dim, *args, _stream()), "dsa_head_weights_proj")
+    return out
+
+
+def out_unabsorb(p: Problem, o_latent, w_uv, out=None, dtype=torch.bfloat16) -> torch.Tensor:
+    """Per-head un-absorption: o_latent [B, Lq, NH, Dv] bf16, w_uv [NH, V, Dv]
+    bf16 -> out [B, Lq, NH, V]; see dsa_out_unabsorb."""
+    V = w_uv.shape[1]
+    if out is None:
+        out = torch.empty(p.batch, p.q_len, p.attn_heads, V, dtype=dtype, device=o_latent.device)
+    args = (_ptr(o_latent, "o_latent", torch.bfloat16, (p.batch, p.q_len, p.attn_heads, p.v_dim)),
+            _ptr(w_uv, "w_uv", torch.bfloat16, (p.attn_heads, V, p.v_dim)),
+            _ptr(out, "out", out.dtype, (p.batch, p.q_len, p.attn_heads, V)))
+    _check(lib().dsa_out_unabsorb(ctypes.byref(p), V, *args, _proj_out_dtype(out.dtype), _stream()),
+           "dsa_out_unabsorb")
+    return out
 
 
 def _out_tensor(p: Problem, device):
