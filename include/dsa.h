@@ -244,9 +244,15 @@ dsa_status_t dsa_index_q_proj(const dsa_problem_t* prob, int32_t q_lora_rank, co
  *   w_proj  [H][dim]
  *   head_w  [B][Lq][H] fp32:  head_w[t][h] = sum_i x[t][i] * w_proj[h][i]
  * (no bias, no extra constant).
+ *   workspace: optional (NULL, 0 allowed), 16-byte aligned, at least
+ *   dsa_head_weights_workspace_size() bytes to be used: few-token calls then
+ *   split the dim range over work-groups and add the partials in a fixed
+ *   order (the result does not depend on whether the workspace is given
+ *   beyond fp32 rounding of a different summation grouping).
  */
 dsa_status_t dsa_head_weights_proj(const dsa_problem_t* prob, int32_t dim, const void* x, const void* w_proj,
-                                   float* head_w, hipStream_t stream);
+                                   float* head_w, void* workspace, size_t workspace_bytes, hipStream_t stream);
+size_t dsa_head_weights_workspace_size(const dsa_problem_t* prob, int32_t dim);
 
 /* Un-absorption of the attention output: the value half of MLA's key/value
  * up-projection applied per head to the latent output (kv_lora_rank 512 and

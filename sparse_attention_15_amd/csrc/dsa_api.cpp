@@ -213,7 +213,7 @@ dsa_status_t forward_impl(const dsa_problem_t* prob, const void* q_idx, const ui
 // Shared checks of the projections: bf16 operands with 16-byte rows.
 dsa_status_t run_gemm(const void* a, const void* b, void* c, int m, int n, int k, int batch, int64_t lda,
                       int64_t ldb, int64_t ldc, int64_t sa, int64_t sb, int64_t sc, dsa_dtype_t c_dtype,
-                      hipStream_t stream) {
+                      hipStream_t stream, void* workspace = nullptr, size_t workspace_bytes = 0) {
   if (!a || !b || !c || k < 8 || (k & 7) || (lda & 7) || (ldb & 7)) return DSA_ERR_INVALID_ARGUMENT;
   if (c_dtype != DSA_BF16 && c_dtype != DSA_F32) return DSA_ERR_INVALID_ARGUMENT;
   if (!aligned16(a) || !aligned16(b) || (reinterpret_cast<uintptr_t>(c) & 3u)) return DSA_ERR_INVALID_ARGUMENT;
@@ -225,6 +225,14 @@ dsa_status_t run_gemm(const void* a, const void* b, void* c, int m, int n, int k
   g.lda = lda; g.ldb = ldb; g.ldc = ldc;
   g.sa = sa; g.sb = sb; g.sc = sc;
   g.c_f32 = c_dtype == DSA_F32;
+  g.part = nullptr;
+  g.ksplit = 1;
+  size_t need = 0;
+  const int ks = gemm_ksplit(m, n, k, batch, &need);
+  if (ks > 1 && workspace && workspace_bytes >= need && aligned16(workspace)) {
+    g.part = static_cast<float*>(workspace);
+    g.ksplit = ks;
+  }
   return hip_status(launch_gemm_bt(g, stream));
 }
 
@@ -361,13 +369,21 @@ dsa_status_t dsa_index_q_proj(const dsa_problem_t* prob, int32_t q_lora_rank, co
 }
 
 dsa_status_t dsa_head_weights_proj(const dsa_problem_t* prob, int32_t dim, const void* x, const void* w_proj,
-                                   float* head_w, hipStream_t stream) {
+                                   float* head_w, void* workspace, size_t workspace_bytes, hipStream_t stream) {
   Path path;
   const dsa_status_t st = check_problem(prob, &path);
   if (st != DSA_OK) return st;
   const dsa_problem_t& p = *prob;
   return run_gemm(x, w_proj, head_w, p.batch * p.q_len, p.index_heads, dim, 1, dim, dim, p.index_heads, 0, 0, 0,
-                  DSA_F32, stream);
+                  DSA_F32, stream, workspace, workspace_bytes);
+}
+
+size_t dsa_head_weights_workspace_size(const dsa_problem_t* prob, int32_t dim) {
+  Path path;
+  if (check_problem(prob, &path) != DSA_OK || dim < 1) return 0;
+  size_t need = 0;
+  gemm_ksplit(prob->batch * prob->q_len, prob->index_heads, dim, 1, &need);
+  return need;
 }
 
 dsa_status_t dsa_out_unabsorb(const dsa_problem_t* prob, int32_t v_head_dim, const void* o_latent, const void* w_uv,

@@ -85,8 +85,13 @@ struct GemmLaunch {
   int64_t lda, ldb, ldc;   // row strides (elements)
   int64_t sa, sb, sc;      // batch strides (elements)
   int c_f32;               // 1: fp32 output, 0: bf16
+  float* part;             // split-K partials [ksplit][batch][M][N] (ksplit > 1)
+  int ksplit;              // 1: no split
 };
 hipError_t launch_gemm_bt(const GemmLaunch& g, hipStream_t s);
+// Split count launch_gemm_bt would use for this shape given room for
+// `avail` bytes of partials (1 = none); writes the bytes it needs.
+int gemm_ksplit(int M, int N, int K, int batch, size_t* bytes);
 
 // Split count the bf16 attention uses for a launch of `rows` queries.
 int attn_splits_bf16(int rows, int K);

@@ -17,10 +17,14 @@
 // banks; the next stage is loaded into registers while the current one is
 // multiplied, one barrier per stage.
 // Skinny kernel (at most 32 rows, the decode shapes, which stream the
-// weights): one 32 x 32 output tile per work-group; its 4 waves take
+// weights): one 32 x 32 output tile per work-group; its 4, 8 or 16 waves take
 // interleaved 64-k stages through private LDS buffers (no barriers in the
-// loop) and add their accumulators through LDS at the end, so four times as
-// many weight loads are in flight per output tile.
+// loop) and add their accumulators through LDS at the end, so that many
+// weight loads are in flight per output tile.  When there are too few
+// output tiles to fill the chip (the head-weight projection: 64 outputs per
+// token over 7168 inputs) and the caller gives a workspace, the k range is
+// also split over work-groups, and a second kernel adds the fp32 partials in
+// split order.
 #include "dsa_device.h"
 #include "dsa_internal.h"
 
@@ -127,14 +131,19 @@ __global__ __launch_bounds__(256) void gemm_tile_kernel(GemmLaunch g) {
     }
 }
 
-__global__ __launch_bounds__(256) void gemm_skinny_kernel(GemmLaunch g) {
+template <int NW>   // waves per work-group, each taking every NW-th stage
+__global__ __launch_bounds__(NW * 64) void gemm_skinny_kernel(GemmLaunch g) {
   // per wave: one stage of A (32 rows) and B (32 rows), 128 bytes per row
-  __shared__ __attribute__((aligned(16))) uint8_t lds[4][64 * 128];
+  __shared__ __attribute__((aligned(16))) uint8_t lds[NW][64 * 128];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int n0 = blockIdx.x * 32;
-  const uint16_t* A = g.A + (int64_t)blockIdx.z * g.sa;
-  const uint16_t* B = g.B + (int64_t)blockIdx.z * g.sb;
-  const int nk = (g.K + kGK - 1) / kGK;
+  const int bz = blockIdx.z / g.ksplit, kz = blockIdx.z - bz * g.ksplit;
+  const uint16_t* A = g.A + (int64_t)bz * g.sa;
+  const uint16_t* B = g.B + (int64_t)bz * g.sb;
+  const int nk_all = (g.K + kGK - 1) / kGK;
+  const int per = (nk_all + g.ksplit - 1) / g.ksplit;   // stages of this split: [k_first, nk)
+  const int k_first = kz * per;
+  const int nk = min(nk_all, k_first + per);
   uint8_t* mine = lds[wave];
 
   u32x4 ra[4], rb[4];
@@ -152,9 +161,9 @@ __global__ __launch_bounds__(256) void gemm_skinny_kernel(GemmLaunch g) {
 #pragma unroll
   for (int e = 0; e < 16; ++e) acc[e] = 0.f;
   const int half = lane >> 5, r32 = lane & 31;
-  int kt = wave;
+  int kt = k_first + wave;
   if (kt < nk) load(kt);
-  for (; kt < nk; kt += 4) {
+  for (; kt < nk; kt += NW) {
     // the previous stage's operand reads were issued before these writes, and
     // one wave's LDS operations complete in order
 #pragma unroll
@@ -163,7 +172,7 @@ __global__ __launch_bounds__(256) void gemm_skinny_kernel(GemmLaunch g) {
       st16(mine + tile_off(f >> 3, f & 7), ra[p]);
       st16(mine + 32 * 128 + tile_off(f >> 3, f & 7), rb[p]);
     }
-    if (kt + 4 < nk) load(kt + 4);
+    if (kt + NW < nk) load(kt + NW);
 #pragma unroll
     for (int s = 0; s < kGK / 16; ++s) {
       const int kc = 2 * s + half;
@@ -172,32 +181,80 @@ __global__ __launch_bounds__(256) void gemm_skinny_kernel(GemmLaunch g) {
       acc = mfma32(av, bv, acc);
     }
   }
-  // sum the four waves' partial tiles: waves 1..3 through LDS
+  // sum the waves' partial tiles through LDS; wave w then finishes the
+  // accumulator entries e = w, w + NW, ...
   __syncthreads();                                // every wave is done with its stage buffer
-  float* red = reinterpret_cast<float*>(&lds[0][0]);   // [3][16][64]
-  if (wave > 0)
+  float* red = reinterpret_cast<float*>(&lds[0][0]);   // [NW][16][64]
 #pragma unroll
-    for (int e = 0; e < 16; ++e) red[((wave - 1) * 16 + e) * 64 + lane] = acc[e];
+  for (int e = 0; e < 16; ++e) red[(wave * 16 + e) * 64 + lane] = acc[e];
   __syncthreads();
-  if (wave == 0) {
-    void* cb = g.c_f32 ? (void*)(static_cast<float*>(g.C) + (int64_t)blockIdx.z * g.sc)
-                       : (void*)(static_cast<uint16_t*>(g.C) + (int64_t)blockIdx.z * g.sc);
-    const int n = n0 + r32;
+  void* cb = g.c_f32 ? (void*)(static_cast<float*>(g.C) + (int64_t)bz * g.sc)
+                     : (void*)(static_cast<uint16_t*>(g.C) + (int64_t)bz * g.sc);
+  float* pp = g.part + ((int64_t)kz * g.batch + bz) * g.M * g.N;   // used when ksplit > 1
+  const int n = n0 + r32;
+  for (int e = wave; e < 16; e += NW) {
+    float v = 0.f;
 #pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      const float v = acc[e] + red[e * 64 + lane] + red[(16 + e) * 64 + lane] + red[(32 + e) * 64 + lane];
-      const int m = 8 * (e >> 2) + 4 * half + (e & 3);
-      if (m < g.M && n < g.N) store_c(g, cb, m, n, v);
+    for (int w = 0; w < NW; ++w) v += red[(w * 16 + e) * 64 + lane];
+    const int m = 8 * (e >> 2) + 4 * half + (e & 3);
+    if (m < g.M && n < g.N) {
+      if (g.ksplit > 1) pp[(int64_t)m * g.N + n] = v;
+      else store_c(g, cb, m, n, v);
     }
   }
 }
 
+// Split-K partials summed in split order (so the result does not depend on
+// scheduling), one thread per output.
+__global__ __launch_bounds__(256) void gemm_split_reduce_kernel(GemmLaunch g) {
+  const int64_t per_b = (int64_t)g.M * g.N;
+  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (idx >= per_b * g.batch) return;
+  const int bz = (int)(idx / per_b);
+  const int64_t mn = idx - bz * per_b;
+  const int m = (int)(mn / g.N), n = (int)(mn - (int64_t)m * g.N);
+  float v = 0.f;
+  for (int kz = 0; kz < g.ksplit; ++kz) v += g.part[((int64_t)kz * g.batch + bz) * per_b + mn];
+  void* cb = g.c_f32 ? (void*)(static_cast<float*>(g.C) + (int64_t)bz * g.sc)
+                     : (void*)(static_cast<uint16_t*>(g.C) + (int64_t)bz * g.sc);
+  store_c(g, cb, m, n, v);
+}
+
 }  // namespace
 
+int gemm_ksplit(int M, int N, int K, int batch, size_t* bytes) {
+  *bytes = 0;
+  if (M > 32) return 1;
+  const int64_t wgs = (int64_t)((N + 31) / 32) * batch;
+  const int nk = (K + kGK - 1) / kGK;
+  if (wgs >= 64 || nk < 16) return 1;
+  // about 128 work-groups, each with at least 4 stages (one per wave)
+  int ks = (int)(128 / wgs);
+  ks = min(ks, nk / 4);
+  if (ks < 2) return 1;
+  *bytes = (size_t)ks * batch * M * N * sizeof(float);
+  return ks;
+}
+
 hipError_t launch_gemm_bt(const GemmLaunch& g, hipStream_t s) {
+  if (g.ksplit > 1) {                            // skinny shapes only (see gemm_ksplit)
+    dim3 grid((g.N + 31) / 32, 1, g.batch * g.ksplit);
+    hipLaunchKernelGGL(gemm_skinny_kernel<4>, grid, dim3(256), 0, s, g);
+    const int64_t outs = (int64_t)g.M * g.N * g.batch;
+    hipLaunchKernelGGL(gemm_split_reduce_kernel, dim3((unsigned)((outs + 255) / 256)), dim3(256), 0, s, g);
+    return hipGetLastError();
+  }
   if (g.M <= 32) {
+    // few output tiles: more waves per tile, so that enough weight loads are
+    // in flight per CU
     dim3 grid((g.N + 31) / 32, 1, g.batch);
-    hipLaunchKernelGGL(gemm_skinny_kernel, grid, dim3(256), 0, s, g);
+    const int64_t wgs = (int64_t)grid.x * g.batch;
+    if (wgs >= 1024)
+      hipLaunchKernelGGL(gemm_skinny_kernel<4>, grid, dim3(256), 0, s, g);
+    else if (wgs >= 64)
+      hipLaunchKernelGGL(gemm_skinny_kernel<8>, grid, dim3(512), 0, s, g);
+    else
+      hipLaunchKernelGGL(gemm_skinny_kernel<16>, grid, dim3(1024), 0, s, g);
   } else if (g.M >= 128 && g.N >= 128) {
     dim3 grid((g.N + 127) / 128, (g.M + 127) / 128, g.batch);
     hipLaunchKernelGGL((gemm_tile_kernel<64, 64>), grid, dim3(256), 0, s, g);

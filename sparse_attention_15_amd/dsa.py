@@ -80,11 +80,13 @@ def lib() -> ctypes.CDLL:
     L.dsa_cache_append.argtypes = [P, ctypes.c_int32] + [ctypes.c_void_p] * 6 + [ctypes.c_void_p]
     L.dsa_cache_append.restype = ctypes.c_int
     for name, extra in (("dsa_index_q_proj", [I32, V, V, V, ctypes.c_int, V]),
-                        ("dsa_head_weights_proj", [I32, V, V, V, V]),
+                        ("dsa_head_weights_proj", [I32, V, V, V, V, SZ, V]),
                         ("dsa_out_unabsorb", [I32, V, V, V, ctypes.c_int, V])):
         f = getattr(L, name)
         f.argtypes = [P] + extra
         f.restype = ctypes.c_int
+    L.dsa_head_weights_workspace_size.argtypes = [P, I32]
+    L.dsa_head_weights_workspace_size.restype = SZ
     L.dsa_status_string.argtypes = [ctypes.c_int]
     L.dsa_status_string.restype = ctypes.c_char_p
     L.dsa_abi_version.argtypes = []
@@ -268,16 +270,27 @@ def index_q_proj(p: Problem, cq, wq_b, out=None, dtype=torch.bfloat16) -> torch.
     return out
 
 
-def head_weights_proj(p: Problem, x, w_proj, out=None) -> torch.Tensor:
+def head_weights_workspace_size(p: Problem, dim: int) -> int:
+    return int(lib().dsa_head_weights_workspace_size(ctypes.byref(p), dim))
+
+
+def head_weights_proj(p: Problem, x, w_proj, out=None, workspace="auto") -> torch.Tensor:
     """Head weights from the hidden state: x [B, Lq, dim] bf16, w_proj [H, dim]
-    bf16 -> head_w [B, Lq, H] fp32; see dsa_head_weights_proj."""
+    bf16 -> head_w [B, Lq, H] fp32; see dsa_head_weights_proj.  workspace:
+    "auto" allocates what dsa_head_weights_workspace_size asks for, None
+    passes none, or a uint8 CUDA tensor."""
     dim = x.shape[-1]
     if out is None:
         out = torch.empty(p.batch, p.q_len, p.index_heads, dtype=torch.float32, device=x.device)
     args = (_ptr(x, "x", torch.bfloat16, (p.batch, p.q_len, dim)),
             _ptr(w_proj, "w_proj", torch.bfloat16, (p.index_heads, dim)),
             _ptr(out, "head_w", torch.float32, (p.batch, p.q_len, p.index_heads)))
-    _check(lib().dsa_head_weights_proj(ctypes.byref(p), dim, *args, _stream()), "dsa_head_weights_proj")
+    if isinstance(workspace, str):
+        n = head_weights_workspace_size(p, dim)
+        workspace = torch.empty(n, dtype=torch.uint8, device=x.device) if n else None
+    wsp = ctypes.c_void_p(workspace.data_ptr()) if workspace is not None else None
+    wsb = workspace.numel() if workspace is not None else 0
+    _check(lib().dsa_head_weights_proj(ctypes.byref(p), dim, *args, wsp, wsb, _stream()), "dsa_head_weights_proj")
     return out
 
 

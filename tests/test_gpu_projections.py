@@ -69,12 +69,13 @@ def test_index_q_proj(name, cfg, R, hid, V, out):
     _check(q, ref, _bound(a, b, R).reshape(q.shape), out == torch.bfloat16)
 
 
+@pytest.mark.parametrize("ws", ["auto", None], ids=["split_k", "no_workspace"])
 @pytest.mark.parametrize("name,cfg,R,hid,V", SMALL, ids=[s[0] for s in SMALL])
-def test_head_weights_proj(name, cfg, R, hid, V):
+def test_head_weights_proj(name, cfg, R, hid, V, ws):
     dsa = _dsa()
     inp = generate_projection_inputs(cfg, device=DEV, q_lora_rank=R, hidden=hid, v_head_dim=V)
     p = dsa.make_problem(cfg)
-    w = dsa.head_weights_proj(p, inp["x"], inp["w_proj"])
+    w = dsa.head_weights_proj(p, inp["x"], inp["w_proj"], workspace=ws)
     torch.cuda.synchronize()
     a = f64(inp["x"]).reshape(-1, hid)
     b = f64(inp["w_proj"])
@@ -135,4 +136,8 @@ def test_bad_arguments_are_rejected():
     assert L.dsa_index_q_proj(ctypes.byref(p), 12, v, v, v, dsa.DSA_BF16, None) == 1
     assert L.dsa_index_q_proj(ctypes.byref(p), 16, None, v, v, dsa.DSA_BF16, None) == 1
     assert L.dsa_out_unabsorb(ctypes.byref(p), 128, v, v, v, dsa.DSA_FP8_E4M3, None) == 1
-    assert L.dsa_head_weights_proj(ctypes.byref(p), 7168, v, None, v, None) == 1
+    assert L.dsa_head_weights_proj(ctypes.byref(p), 7168, v, None, v, None, 0, None) == 1
+    # decode shape: the split plan asks for partials; a short workspace is
+    # not an error (the call runs unsplit)
+    assert dsa.head_weights_workspace_size(p, 7168) > 0
+    assert dsa.head_weights_workspace_size(dsa.make_problem(C.PREFILL_8K), 7168) == 0
