@@ -75,7 +75,9 @@ size_t attn_partials_bytes(const dsa_problem_t& p, int rows, int splits) {
 struct ForwardPlan {
   int chunk;       // queries per chunk
   int n_chunks;
-  size_t scores_bytes, idx_bytes, part_bytes;
+  int tk_slices, tk_slice_len;   // two-stage top-k (tk_slices > 1)
+  size_t scores_bytes, idx_bytes, part_bytes, cand_bytes;
+  size_t total() const { return scores_bytes + idx_bytes + part_bytes + cand_bytes; }
 };
 
 ForwardPlan plan_forward(const dsa_problem_t& p, Path path, bool need_idx) {
@@ -86,6 +88,8 @@ ForwardPlan plan_forward(const dsa_problem_t& p, Path path, bool need_idx) {
   f.idx_bytes = need_idx ? align_up((size_t)p.batch * p.q_len * p.topk * 4) : 0;
   const int rows = p.batch * f.chunk;
   f.part_bytes = attn_partials_bytes(p, rows, attn_splits(p, path, rows));
+  f.tk_slices = topk_slices(rows, p.kv_len, p.topk, &f.tk_slice_len);
+  f.cand_bytes = f.tk_slices > 1 ? align_up((size_t)rows * f.tk_slices * p.topk * 4) : 0;
   return f;
 }
 
@@ -107,6 +111,7 @@ TopkLaunch make_topk(const dsa_problem_t& p, const float* scores, int64_t row_st
   a.B = p.batch; a.Lq = p.q_len; a.Lk = p.kv_len; a.K = p.topk;
   a.q_begin = q_begin; a.q_count = q_count;
   a.vec_ok = aligned16(scores) && (row_stride % 4) == 0;
+  a.slices = 1; a.slice_len = 0; a.cand = nullptr;
   return a;
 }
 
@@ -172,7 +177,7 @@ dsa_status_t forward_impl(const dsa_problem_t* prob, const void* q_idx, const ui
   if ((st = check_attn_ptrs(q_attn, kv, out)) != DSA_OK) return st;
   if ((topk_idx && !aligned16(topk_idx)) || (lse && !aligned16(lse))) return DSA_ERR_INVALID_ARGUMENT;
   const ForwardPlan f = plan_forward(p, path, topk_idx == nullptr);
-  const size_t need = f.scores_bytes + f.idx_bytes + f.part_bytes;
+  const size_t need = f.total();
   if (workspace_bytes < need) return DSA_ERR_WORKSPACE_TOO_SMALL;
   if (!workspace || !aligned16(workspace)) return DSA_ERR_INVALID_ARGUMENT;
   if (n_chunks_out) *n_chunks_out = f.n_chunks;
@@ -181,6 +186,7 @@ dsa_status_t forward_impl(const dsa_problem_t* prob, const void* q_idx, const ui
   float* scores = reinterpret_cast<float*>(ws);
   int32_t* idx = topk_idx ? topk_idx : reinterpret_cast<int32_t*>(ws + f.scores_bytes);
   void* part = ws + f.scores_bytes + f.idx_bytes;
+  int32_t* cand = reinterpret_cast<int32_t*>(ws + f.scores_bytes + f.idx_bytes + f.part_bytes);
 
   for (int c = 0; c < f.n_chunks; ++c) {
     const int q0 = c * f.chunk;
@@ -193,7 +199,13 @@ dsa_status_t forward_impl(const dsa_problem_t* prob, const void* q_idx, const ui
     if ((e = ev.rec(c, 0, 1)) != hipSuccess) return DSA_ERR_HIP;
     // 2. top-k
     if ((e = ev.rec(c, 1, 0)) != hipSuccess) return DSA_ERR_HIP;
-    if ((e = launch_topk(make_topk(p, scores, p.kv_len, idx, q0, qn), stream)) != hipSuccess) return hip_status(e);
+    TopkLaunch ta = make_topk(p, scores, p.kv_len, idx, q0, qn);
+    if (f.tk_slices > 1) {
+      ta.slices = f.tk_slices;
+      ta.slice_len = f.tk_slice_len;
+      ta.cand = cand;
+    }
+    if ((e = launch_topk(ta, stream)) != hipSuccess) return hip_status(e);
     if ((e = ev.rec(c, 1, 1)) != hipSuccess) return DSA_ERR_HIP;
     // 3. attention (+ combine); every chunk uses the split count the
     //    workspace was sized for (that of a full chunk)
@@ -315,7 +327,7 @@ size_t dsa_workspace_size(const dsa_problem_t* prob, int32_t op) {
   }
   if (op == DSA_OP_FORWARD) {
     const ForwardPlan f = plan_forward(p, path, true);
-    return f.scores_bytes + f.idx_bytes + f.part_bytes;
+    return f.total();
   }
   return 0;
 }

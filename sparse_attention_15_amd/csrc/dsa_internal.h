@@ -30,6 +30,10 @@ struct TopkLaunch {
   int B, Lq, Lk, K;
   int q_begin, q_count;
   int vec_ok;              // rows are 16-byte aligned: use 16-byte loads
+  // two-stage selection (slices > 1): each row's slices of slice_len
+  // positions first keep their own top K in cand [rows][slices][K]
+  int slices, slice_len;
+  int32_t* cand;
 };
 
 struct AttnLaunch {
@@ -69,6 +73,9 @@ hipError_t launch_rotate_quant(const void* x, int f32_in, int64_t rows, uint8_t*
 
 // Top-k (all dtypes: scores are fp32).
 hipError_t launch_topk(const TopkLaunch& a, hipStream_t s);
+// Slices per row for a two-stage selection over `rows` rows of up to n_max
+// positions (1 = single stage); writes the slice length.
+int topk_slices(int rows, int n_max, int K, int* slice_len);
 
 // Sparse MLA.  *_bf16 needs NH = 128, Dqk = 576, Dv = 512.
 hipError_t launch_attn_f32(const AttnLaunch& a, hipStream_t s);

@@ -127,23 +127,56 @@ __device__ void find_bin(Shared<NC, C>& sh, int nb, uint32_t k) {
   __syncthreads();
 }
 
+// Modes: kRows selects from score rows; kSlice (first of two stages for a
+// few long rows) selects the top K of each slice of a row into a candidate
+// list; kCand (second stage) selects from a row's candidate lists, reading
+// each candidate's score through its position.
+enum { kRows = 0, kSlice = 1, kCand = 2 };
+
 // NC 16-byte chunks per thread kept in registers (0 = re-read each pass);
 // C histogram copies.
-template <int NC, int C>
+template <int NC, int C, int MODE>
 __global__ __launch_bounds__(kThreads) void topk_kernel(TopkLaunch a) {
   __shared__ Shared<NC, C> sh;
   constexpr int S = Shared<NC, C>::kStride;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int row = gridDim.x - 1 - blockIdx.x;     // longest rows first
+  const int r = gridDim.x - 1 - blockIdx.x;       // longest rows first
+  const int row = MODE == kSlice ? r / a.slices : r;
+  const int slice = MODE == kSlice ? r - row * a.slices : 0;
   const int b = row / a.q_count;
   const int i = a.q_begin + row % a.q_count;
-  const int n = a.Lk - a.Lq + i + 1;
+  const int n_row = a.Lk - a.Lq + i + 1;          // visible keys of this query
   const int K = a.K;
-  int32_t* out = a.out + ((int64_t)b * a.Lq + i) * K;
   const float* src = a.scores + (int64_t)row * a.row_stride;
+  const int p0 = slice * a.slice_len;             // first position of the slice
+  int n;                                          // elements to select from
+  int32_t* out;
+  const int32_t* cand = nullptr;                  // kCand: this row's candidate positions
+  if constexpr (MODE == kRows) {
+    n = n_row;
+    out = a.out + ((int64_t)b * a.Lq + i) * K;
+  } else if constexpr (MODE == kSlice) {
+    n = max(0, min(a.slice_len, n_row - p0));
+    src += p0;
+    out = a.cand + ((int64_t)row * a.slices + slice) * K;
+  } else {
+    n = a.slices * K;
+    cand = a.cand + (int64_t)row * a.slices * K;
+    out = a.out + ((int64_t)b * a.Lq + i) * K;
+  }
+  // position of element x of this selection in the row
+  auto pos_of = [&](int x) -> int32_t {
+    if constexpr (MODE == kSlice) return p0 + x;
+    else if constexpr (MODE == kCand) return cand[x];
+    else return x;
+  };
 
-  if (n <= K) {
-    for (int j = tid; j < K; j += kThreads) out[j] = j < n ? j : -1;
+  if (MODE == kCand && n_row <= K) {             // the whole row is chosen
+    for (int j = tid; j < K; j += kThreads) out[j] = j < n_row ? j : -1;
+    return;
+  }
+  if (n <= K) {                                   // kCand never: n = slices * K > K
+    for (int j = tid; j < K; j += kThreads) out[j] = j < n ? pos_of(j) : -1;
     return;
   }
   const int nchunks = (n + 3) >> 2;               // 4 positions per chunk
@@ -152,15 +185,30 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(TopkLaunch a) {
   auto load_keys = [&](int c, uint32_t (&kk)[4]) {
     const int ch = c * kThreads + tid;
     const int pos = ch * 4;
-    if (a.vec_ok && pos + 3 < n) {
-      const f32x4 v = *reinterpret_cast<const f32x4*>(src + pos);
-      kk[0] = order_key(v.x);
-      kk[1] = order_key(v.y);
-      kk[2] = order_key(v.z);
-      kk[3] = order_key(v.w);
-    } else {
+    if constexpr (MODE == kCand) {
+      // candidates: a position, or -1 for an unused slot (key 0: never chosen)
+      if (a.vec_ok && pos + 3 < n) {
+        const u32x4 cv = ld16(cand + pos);
 #pragma unroll
-      for (int e = 0; e < 4; ++e) kk[e] = (pos + e < n) ? order_key(src[pos + e]) : 0u;
+        for (int e = 0; e < 4; ++e) kk[e] = (int32_t)cv[e] >= 0 ? order_key(src[(int32_t)cv[e]]) : 0u;
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int32_t cx = pos + e < n ? cand[pos + e] : -1;
+          kk[e] = cx >= 0 ? order_key(src[cx]) : 0u;
+        }
+      }
+    } else {
+      if (a.vec_ok && pos + 3 < n) {
+        const f32x4 v = *reinterpret_cast<const f32x4*>(src + pos);
+        kk[0] = order_key(v.x);
+        kk[1] = order_key(v.y);
+        kk[2] = order_key(v.z);
+        kk[3] = order_key(v.w);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) kk[e] = (pos + e < n) ? order_key(src[pos + e]) : 0u;
+      }
     }
   };
 
@@ -292,7 +340,7 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(TopkLaunch a) {
       uint32_t slot = g_b + min(e_b, k_rem);
       const int base = 32 * (tid * J + j);
       while (sel != 0u) {
-        put(slot++, base + __builtin_ctz(sel));
+        put(slot++, pos_of(base + __builtin_ctz(sel)));
         sel &= sel - 1u;
       }
       g_b += __builtin_popcount(gw[j]);
@@ -342,7 +390,7 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(TopkLaunch a) {
             const uint32_t m = kk[g][e] & mask;
             const bool valid = kk[g][e] != 0u;
             const bool gt = valid && m > prefix, eq = valid && m == prefix;
-            if (gt || (eq && e_b < k_rem)) put(g_b + min(e_b, k_rem), pos0 + e);
+            if (gt || (eq && e_b < k_rem)) put(g_b + min(e_b, k_rem), pos_of(pos0 + e));
             g_b += gt ? 1u : 0u;
             e_b += eq ? 1u : 0u;
           }
@@ -374,22 +422,53 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(TopkLaunch a) {
 
 }  // namespace
 
-hipError_t launch_topk(const TopkLaunch& a, hipStream_t s) {
-  const int rows = a.B * a.q_count;
-  const int n_max = a.Lk - a.Lq + a.q_begin + a.q_count;
+namespace {
+
+template <int MODE>
+void launch_mode(const TopkLaunch& a, int n_max, int grid, hipStream_t s) {
   const int chunks = (n_max + 3) / 4;
   const int iters = (chunks + kThreads - 1) / kThreads;
-  dim3 grid(rows), block(kThreads);
   // short rows come in large numbers (prefill): small histograms keep two
   // work-groups per CU; long rows are few and get the widest spreading
   if (iters <= 2)
-    hipLaunchKernelGGL((topk_kernel<2, 2>), grid, block, 0, s, a);
+    hipLaunchKernelGGL((topk_kernel<2, 2, MODE>), dim3(grid), dim3(kThreads), 0, s, a);
   else if (iters <= 8)
-    hipLaunchKernelGGL((topk_kernel<8, 8>), grid, block, 0, s, a);
+    hipLaunchKernelGGL((topk_kernel<8, 8, MODE>), dim3(grid), dim3(kThreads), 0, s, a);
   else if (iters <= 16)
-    hipLaunchKernelGGL((topk_kernel<16, 8>), grid, block, 0, s, a);
-  else
-    hipLaunchKernelGGL((topk_kernel<0, 8>), grid, block, 0, s, a);
+    hipLaunchKernelGGL((topk_kernel<16, 8, MODE>), dim3(grid), dim3(kThreads), 0, s, a);
+  else if constexpr (MODE != kCand)              // candidate rows are at most 65536 long
+    hipLaunchKernelGGL((topk_kernel<0, 8, MODE>), dim3(grid), dim3(kThreads), 0, s, a);
+}
+
+}  // namespace
+
+int topk_slices(int rows, int n_max, int K, int* slice_len) {
+  *slice_len = 0;
+  // one work-group per row keeps one CU's VALU busy over the whole row; with
+  // fewer rows than CUs, split long rows: slices of about sqrt(n K)
+  // positions (stage 1 and stage 2 then each see a similar count).  Each
+  // stage has a fixed cost of a few microseconds (passes, barriers), so
+  // rows below 65536 positions stay single-stage (measured: 32768-position
+  // decode rows take 19.7 us in one stage, 24.6 us in two; 131072-position
+  // rows 82 us in one, 42 us in two).
+  if (rows >= 256 || K > 4096 || (K & 3) || n_max < 4 * K || n_max < 65536) return 1;
+  int len = 4096;
+  while ((int64_t)len * len < (int64_t)n_max * K) len *= 2;
+  const int sl = (n_max + len - 1) / len;
+  if (sl < 2 || (int64_t)sl * K > 65536) return 1;
+  *slice_len = len;
+  return sl;
+}
+
+hipError_t launch_topk(const TopkLaunch& a, hipStream_t s) {
+  const int rows = a.B * a.q_count;
+  const int n_max = a.Lk - a.Lq + a.q_begin + a.q_count;
+  if (a.slices > 1) {
+    launch_mode<kSlice>(a, a.slice_len, rows * a.slices, s);
+    launch_mode<kCand>(a, a.slices * a.K, rows, s);
+  } else {
+    launch_mode<kRows>(a, n_max, rows, s);
+  }
   return hipGetLastError();
 }
 

@@ -157,6 +157,24 @@ def test_topk_special_rows(kind, Lk, K):
         assert np.array_equal(got[0, i], ref), (kind, i)
 
 
+@pytest.mark.parametrize("B,Lq,Lk", [(2, 1, 65536), (3, 1, 70001), (1, 1, 131072), (1, 3, 100000), (2, 2, 80000)])
+def test_two_stage_topk_in_forward_equals_single_stage(B, Lq, Lk):
+    """Few rows of 65536 positions or more: dsa_forward selects in two stages
+    (per-slice top-K, then top-K of the candidates).  Its indices must equal the single-stage
+    selection of dsa_topk over the same scores, bit for bit."""
+    dsa = _dsa()
+    cfg = C.scaled(C.DECODE_32K, batch=B, q_len=Lq, kv_len=Lk, plant_count=min(300, Lk // 100))
+    inp = generate(cfg, device=DEV)
+    p = dsa.make_problem(cfg)
+    scores = dsa.index_scores(p, inp["q_idx"], inp["q_scale"], inp["k_idx"], inp["k_scale"], inp["head_w"])
+    single = dsa.topk(p, scores)
+    idx = torch.empty(B, Lq, cfg.topk, dtype=torch.int32, device=DEV)
+    dsa.forward(p, inp["q_idx"], inp["q_scale"], inp["k_idx"], inp["k_scale"], inp["head_w"], inp["q_attn"],
+                inp["kv"], topk_idx=idx)
+    torch.cuda.synchronize()
+    assert torch.equal(idx, single)
+
+
 def _oracle_sets(cfg, host):
     qf, kf = O.as_f64_index_inputs(host["q_idx"], host["q_scale"], host["k_idx"], host["k_scale"])
     sc = O.index_scores(qf, kf, host["head_w"], cfg.q_len, cfg.kv_len)
