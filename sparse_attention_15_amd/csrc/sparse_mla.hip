@@ -270,16 +270,32 @@ __device__ __forceinline__ void attn_block(AttnState& st, const uint8_t* buf, ui
   st.l_run += lsum;
 }
 
+// NST stage buffers (NST - 1 blocks in flight) and a list window of MAXPER
+// entries.  LDS holds 3 buffers next to a 2048-entry window, or 4 next to a
+// 256-entry one: decode splits have short windows and their gathers are
+// random HBM rows, so they keep one more block in flight, and every wave
+// stages its Q rows at once.
+template <int NST, int MAXPER>
 __global__ __launch_bounds__(kWavesA * 64, 1) void attn_bf16_kernel(AttnLaunch a) {
-  __shared__ __attribute__((aligned(16))) uint8_t stg[3 * kStageBytes];
-  __shared__ __attribute__((aligned(16))) uint32_t spos[kMaxPer];
-  __shared__ uint32_t bmask[kMaxPer / kBK];       // per 32-entry block: bit j = entry j usable
+  static_assert((NST == 3 || NST == 4) && MAXPER % (kWavesA * 64) == 0, "stage / window shape");
+  __shared__ __attribute__((aligned(16))) uint8_t stg[NST * kStageBytes];
+  __shared__ __attribute__((aligned(16))) uint32_t spos[MAXPER];
+  __shared__ uint32_t bmask[MAXPER / kBK];        // per 32-entry block: bit j = entry j usable
   __shared__ int s_lastw[kWavesA];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int hf = lane >> 5, c32 = lane & 31;
-  const int split = blockIdx.x;
-  const int rr = gridDim.y - 1 - blockIdx.y;    // launch row; latest queries first
+  int split = blockIdx.x;
+  int rr = gridDim.y - 1 - blockIdx.y;          // launch row; latest queries first
+  if (a.splits > 1 && (gridDim.y & 7) == 0) {
+    // Work-groups are dealt to the 8 XCDs round-robin by linear id, so ids
+    // x, x+8, x+16, ... share an L2: give them all splits of rows x, x+8, ...
+    // (the splits of a query then fetch its Q rows into one L2 once).
+    const int lin = blockIdx.x + gridDim.x * blockIdx.y;
+    const int loc = lin >> 3;
+    rr = (lin & 7) + 8 * (loc / a.splits);
+    split = loc - (loc / a.splits) * a.splits;
+  }
   const int b = rr / a.q_count;
   const int i = a.q_begin + rr % a.q_count;
   const int64_t qrow = (int64_t)b * a.Lq + i;
@@ -289,10 +305,11 @@ __global__ __launch_bounds__(kWavesA * 64, 1) void attn_bf16_kernel(AttnLaunch a
 
   // This split's list entries (all loads in flight at once), then the Q rows
   // of this wave's 32 heads as one 32-row gather into a stage buffer (whole
-  // cache lines; read back with the key rows' conflict-free addressing):
-  // waves 0-2 now into buffers 0-2, wave 3 after the first barrier into
-  // buffer 2, while blocks 0 and 1 are gathered into buffers 0 and 1.
-  constexpr int kFillIt = kMaxPer / (kWavesA * 64);
+  // cache lines; read back with the key rows' conflict-free addressing).
+  // Four buffers: every wave now, into its own buffer.  Three: waves 0-2 now
+  // into buffers 0-2, wave 3 after the first barrier into buffer 2, while
+  // blocks 0 and 1 are gathered into buffers 0 and 1.
+  constexpr int kFillIt = MAXPER / (kWavesA * 64);
   int pv[kFillIt];
   const int32_t* idx = a.idx + qrow * a.K + j0;
 #pragma unroll
@@ -314,7 +331,7 @@ __global__ __launch_bounds__(kWavesA * 64, 1) void attn_bf16_kernel(AttnLaunch a
       lds_dma16<false>(qwave, off, dst + k * 1024);
     }
   };
-  if (wave < 3) gather_q(wave);
+  if (NST == 4 || wave < 3) gather_q(wave);
   // Chosen rows into LDS as byte offsets (row * 1152; skipped and padding
   // entries point at row 0), one validity bit per entry in bmask (bit j of
   // word w: entry 32w + j is usable), and each wave's last usable entry.
@@ -358,7 +375,7 @@ __global__ __launch_bounds__(kWavesA * 64, 1) void attn_bf16_kernel(AttnLaunch a
 #pragma unroll
     for (int t = 0; t < kQSteps; ++t) st.qf[t] = ld16(qbuf + qk_off[t & 1] + 64 * (t >> 1));
   };
-  if (wave < 3) {
+  if (NST == 4 || wave < 3) {
     wait_vmcnt<0>();                              // this wave's Q rows have landed
     read_q(wave);
   }
@@ -383,7 +400,7 @@ __global__ __launch_bounds__(kWavesA * 64, 1) void attn_bf16_kernel(AttnLaunch a
   __syncthreads();
   const int last = max(max(s_lastw[0], s_lastw[1]), max(s_lastw[2], s_lastw[3]));
   const int nblk = (last + kBK) / kBK;            // blocks up to the last listed entry
-  if (wave == 3) gather_q(2);                     // wave 2 has read its Q from buffer 2
+  if (NST == 3 && wave == 3) gather_q(2);        // wave 2 has read its Q from buffer 2
 
   // Gather map: instruction k of this wave fills LDS chunk slots
   // f = (dma_first(wave) + k)*64 + lane: row f/76, stored chunk f%76, which
@@ -413,20 +430,22 @@ __global__ __launch_bounds__(kWavesA * 64, 1) void attn_bf16_kernel(AttnLaunch a
     for (int k = 0; k < kDmaMax; ++k)
       if (k < dcount) dma16(kvb, roff[k], dma_map[k], __builtin_amdgcn_readfirstlane(dst + (dfirst + k) * 1024));
   };
-  // Block blk lives in stage buffer blk % 3.  Wait for its gather (the next
-  // block's may stay in flight) and barrier: every wave is then also done with
-  // block blk-1, whose buffer receives block blk+2, gathered from inside
-  // block blk's QK steps.
-  if (nblk > 0) issue(0, 0);
-  if (nblk > 1) issue(1, 1);
-  if (wave == 3) {                                // Q rows are older than the block gathers
+  // Block blk lives in stage buffer blk % NST.  Wait for its gather (later
+  // blocks' may stay in flight) and barrier: every wave is then also done
+  // with block blk-1, whose buffer receives block blk+NST-1, gathered from
+  // inside block blk's QK steps.
+#pragma unroll
+  for (int j = 0; j < NST - 1; ++j)
+    if (nblk > j) issue(j, j);
+  if (NST == 3 && wave == 3) {                    // Q rows are older than the block gathers
     if (nblk > 1) wait_vmcnt<18>();
     else if (nblk > 0) wait_vmcnt<9>();
     else wait_vmcnt<0>();
     read_q(2);
   }
   // Consume the Q fragments here so that their LDS reads are complete before
-  // the loop (block 2 is gathered into buffer 2 during block 0).
+  // the loop (with three buffers, block 2 is gathered into buffer 2, wave
+  // 3's Q staging, during block 0).
 #pragma unroll
   for (int t = 0; t < kQSteps; ++t) asm volatile("" : "+v"(st.qf[t]));
   int sb = 0;
@@ -435,7 +454,12 @@ __global__ __launch_bounds__(kWavesA * 64, 1) void attn_bf16_kernel(AttnLaunch a
   g.dfirst = dfirst;
   g.dcount = dcount;
   for (int blk = 0; blk < nblk; ++blk) {
-    if (blk + 1 < nblk) {
+    // block blk has landed once at most `ahead` later blocks are in flight
+    const int ahead = min(nblk - 1 - blk, NST - 2);
+    if (ahead == 2) {
+      if (dcount == 10) wait_vmcnt<20>();
+      else wait_vmcnt<18>();
+    } else if (ahead == 1) {
       if (dcount == 10) wait_vmcnt<10>();
       else wait_vmcnt<9>();
     } else {
@@ -444,13 +468,13 @@ __global__ __launch_bounds__(kWavesA * 64, 1) void attn_bf16_kernel(AttnLaunch a
     __builtin_amdgcn_s_waitcnt(0xc07f);           // lgkmcnt(0)
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
-    const int sn = sb == 0 ? 2 : sb - 1;          // buffer of blocks blk-1 and blk+2
-    g.active = blk + 2 < nblk;
-    g.bp = spos + (blk + 2) * kBK;
+    const int sn = sb == 0 ? NST - 1 : sb - 1;     // buffer of blocks blk-1 and blk+NST-1
+    g.active = blk + NST - 1 < nblk;
+    g.bp = spos + (blk + NST - 1) * kBK;
     g.dst = __builtin_amdgcn_readfirstlane(stg_lds + sn * kStageBytes);
     const uint32_t vmask = __builtin_amdgcn_readfirstlane(bmask[blk]);
     attn_block(st, stg + sb * kStageBytes, vmask, qk_off, pv_off, hf, zscale, g, dma_map);
-    sb = sb == 2 ? 0 : sb + 1;
+    sb = sb == NST - 1 ? 0 : sb + 1;
   }
 
   const float l_tot = st.l_run + shfl_xor(st.l_run, 32);
@@ -519,7 +543,14 @@ __global__ __launch_bounds__(kWavesA * 64, 1) void attn_bf16_kernel(AttnLaunch a
 // thread's loads are in flight together.
 template <int S>
 __global__ __launch_bounds__(256) void attn_combine_kernel(AttnLaunch a) {
-  const int h = blockIdx.x, rr = blockIdx.y, v = threadIdx.x * 4;
+  int h = blockIdx.x, rr = blockIdx.y;
+  const int v = threadIdx.x * 4;
+  if ((gridDim.y & 7) == 0) {                   // row rr on the XCD its splits ran on
+    const int lin = blockIdx.x + gridDim.x * blockIdx.y;
+    const int loc = lin >> 3;
+    rr = (lin & 7) + 8 * (loc / gridDim.x);
+    h = loc - (loc / gridDim.x) * gridDim.x;
+  }
   const int NH = a.NH, Dv = a.Dv;
   const int b = rr / a.q_count;
   const int i = a.q_begin + rr % a.q_count;
@@ -635,7 +666,11 @@ int attn_splits_bf16(int rows, int K) {
 
 hipError_t launch_attn_bf16(const AttnLaunch& a, hipStream_t s) {
   dim3 grid(a.splits, a.B * a.q_count);
-  hipLaunchKernelGGL(attn_bf16_kernel, grid, dim3(kWavesA * 64), 0, s, a);
+  const int per = ((a.K + a.splits - 1) / a.splits + kBK - 1) / kBK * kBK;
+  if (per <= 256)
+    hipLaunchKernelGGL((attn_bf16_kernel<4, 256>), grid, dim3(kWavesA * 64), 0, s, a);
+  else
+    hipLaunchKernelGGL((attn_bf16_kernel<3, kMaxPer>), grid, dim3(kWavesA * 64), 0, s, a);
   return hipGetLastError();
 }
 
