@@ -538,41 +538,44 @@ __global__ __launch_bounds__(kWavesA * 64, 1) void attn_bf16_kernel(AttnLaunch a
 }
 
 // Merge split partials: out = sum_s exp(lse_s - LSE) * O_s, LSE = log sum_s exp(lse_s).
-// grid (NH, rows), Dv/4 threads; partials in the output's precision.  S (the
-// split count, a power of two) is a template parameter so that all of a
-// thread's loads are in flight together.
-template <int S>
+// grid (NH / 4, rows), 256 threads: 64 per head, 8 value dims (one 16-byte
+// bf16 load, or two fp32 ones, per split) per thread; partials in the
+// output's precision.  S (the split count, a power of two) is a template
+// parameter so that all of a thread's loads are in flight together.
+template <int S, bool F32>
 __global__ __launch_bounds__(256) void attn_combine_kernel(AttnLaunch a) {
-  int h = blockIdx.x, rr = blockIdx.y;
-  const int v = threadIdx.x * 4;
+  int hx = blockIdx.x, rr = blockIdx.y;
   if ((gridDim.y & 7) == 0) {                   // row rr on the XCD its splits ran on
     const int lin = blockIdx.x + gridDim.x * blockIdx.y;
     const int loc = lin >> 3;
     rr = (lin & 7) + 8 * (loc / gridDim.x);
-    h = loc - (loc / gridDim.x) * gridDim.x;
+    hx = loc - (loc / gridDim.x) * gridDim.x;
   }
+  const int h = 4 * hx + (threadIdx.x >> 6), v = 8 * (threadIdx.x & 63);
   const int NH = a.NH, Dv = a.Dv;
   const int b = rr / a.q_count;
   const int i = a.q_begin + rr % a.q_count;
   const int64_t qrow = (int64_t)b * a.Lq + i;
   const float* pl = a.part_lse + (int64_t)rr * S * NH + h;
   float ls[S];
-  f32x4 po[S];
+  f32x4 pf[F32 ? S : 1][2];                       // fp32 partials
+  u32x4 pb[F32 ? 1 : S];                          // bf16 partials
 #pragma unroll
   for (int s = 0; s < S; ++s) {
     ls[s] = pl[(int64_t)s * NH];
     const int64_t off = (((int64_t)rr * S + s) * NH + h) * Dv + v;
-    if (a.out_f32) {
-      po[s] = *reinterpret_cast<const f32x4*>(static_cast<const float*>(a.part_o) + off);
+    if constexpr (F32) {
+      const f32x4* q = reinterpret_cast<const f32x4*>(static_cast<const float*>(a.part_o) + off);
+      pf[s][0] = q[0];
+      pf[s][1] = q[1];
     } else {
-      const u32x2 pb = *reinterpret_cast<const u32x2*>(static_cast<const uint16_t*>(a.part_o) + off);
-      po[s] = f32x4{bf16_lo(pb[0]), bf16_hi(pb[0]), bf16_lo(pb[1]), bf16_hi(pb[1])};
+      pb[s] = ld16(static_cast<const uint16_t*>(a.part_o) + off);
     }
   }
   float m = kNegInf;
 #pragma unroll
   for (int s = 0; s < S; ++s) m = fmaxf(m, ls[s]);
-  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   float sum = 0.f;
   if (m != kNegInf) {
 #pragma unroll
@@ -580,17 +583,28 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnLaunch a) {
       if (ls[s] == kNegInf) continue;             // an empty split holds zeros
       const float wgt = __expf(ls[s] - m);
       sum += wgt;
-      acc += wgt * po[s];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        float x;
+        if constexpr (F32) x = pf[s][e >> 2][e & 3];
+        else x = (e & 1) ? bf16_hi(pb[s][e >> 1]) : bf16_lo(pb[s][e >> 1]);
+        acc[e] += wgt * x;
+      }
     }
-    acc *= 1.f / sum;
+    const float inv = 1.f / sum;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[e] *= inv;
   }
-  if (a.out_f32) {
-    *reinterpret_cast<f32x4*>(static_cast<float*>(a.out) + (qrow * NH + h) * Dv + v) = acc;
+  if constexpr (F32) {
+    float* o = static_cast<float*>(a.out) + (qrow * NH + h) * Dv + v;
+    *reinterpret_cast<f32x4*>(o) = f32x4{acc[0], acc[1], acc[2], acc[3]};
+    *reinterpret_cast<f32x4*>(o + 4) = f32x4{acc[4], acc[5], acc[6], acc[7]};
   } else {
-    u32x2 v2 = {pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3])};
-    *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(a.out) + (qrow * NH + h) * Dv + v) = v2;
+    st16(static_cast<uint16_t*>(a.out) + (qrow * NH + h) * Dv + v,
+         u32x4{pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3]), pack_bf16x2(acc[4], acc[5]),
+               pack_bf16x2(acc[6], acc[7])});
   }
-  if (a.lse && threadIdx.x == 0) a.lse[qrow * NH + h] = m == kNegInf ? kNegInf : m + __logf(sum);
+  if (a.lse && (threadIdx.x & 63) == 0) a.lse[qrow * NH + h] = m == kNegInf ? kNegInf : m + __logf(sum);
 }
 
 // ------------------------------------------------------------- fp32 -------
@@ -674,18 +688,25 @@ hipError_t launch_attn_bf16(const AttnLaunch& a, hipStream_t s) {
   return hipGetLastError();
 }
 
-hipError_t launch_attn_combine(const AttnLaunch& a, hipStream_t s) {
-  dim3 grid(a.NH, a.B * a.q_count);
-  dim3 block(a.Dv / 4);
+template <bool F32>
+hipError_t launch_combine_t(const AttnLaunch& a, hipStream_t s) {
+  dim3 grid(a.NH / 4, a.B * a.q_count);
+  dim3 block(256);
   switch (a.splits) {
-    case 2: hipLaunchKernelGGL(attn_combine_kernel<2>, grid, block, 0, s, a); break;
-    case 4: hipLaunchKernelGGL(attn_combine_kernel<4>, grid, block, 0, s, a); break;
-    case 8: hipLaunchKernelGGL(attn_combine_kernel<8>, grid, block, 0, s, a); break;
-    case 16: hipLaunchKernelGGL(attn_combine_kernel<16>, grid, block, 0, s, a); break;
-    case 32: hipLaunchKernelGGL(attn_combine_kernel<32>, grid, block, 0, s, a); break;
+    case 2: hipLaunchKernelGGL((attn_combine_kernel<2, F32>), grid, block, 0, s, a); break;
+    case 4: hipLaunchKernelGGL((attn_combine_kernel<4, F32>), grid, block, 0, s, a); break;
+    case 8: hipLaunchKernelGGL((attn_combine_kernel<8, F32>), grid, block, 0, s, a); break;
+    case 16: hipLaunchKernelGGL((attn_combine_kernel<16, F32>), grid, block, 0, s, a); break;
+    case 32: hipLaunchKernelGGL((attn_combine_kernel<32, F32>), grid, block, 0, s, a); break;
     default: return hipErrorInvalidValue;       // splits are powers of two up to 32
   }
   return hipGetLastError();
+}
+
+// bf16 kernel shapes only: NH = 128, Dv = 512 (64 threads x 8 dims per head)
+hipError_t launch_attn_combine(const AttnLaunch& a, hipStream_t s) {
+  if (a.NH % 4 != 0 || a.Dv != 512) return hipErrorInvalidValue;
+  return a.out_f32 ? launch_combine_t<true>(a, s) : launch_combine_t<false>(a, s);
 }
 
 hipError_t launch_attn_f32(const AttnLaunch& a, hipStream_t s) {
