@@ -105,12 +105,13 @@ def kernel_units(cfg, kernel, al, n_chunks, split_rows):
                     "algorithmic bytes per launch: selected latent rows + q + out + lse")
         return ("mfma", al["attn_flops"] / n_chunks, "TFLOP/s", MFMA_BF16_PEAK_TFLOPS,
                 "algorithmic flops per launch: 2*NH*(Dqk+Dv) per selected (query, key) pair")
-    # combine: read the fp32 partials of every split, write out and lse
+    # combine: read the partials (output precision) and LSEs of every split,
+    # write out and lse
     ob = 4 if cfg.index_dtype == "f32" else 2
     rows = B * Lq / n_chunks
-    byts = rows * NH * (split_rows * (Dv * 4 + 4) + Dv * ob + 4)
+    byts = rows * NH * (split_rows * (Dv * ob + 4) + Dv * ob + 4)
     return ("hbm", byts, "GB/s", HBM_PEAK_GBS,
-            "bytes per launch: fp32 split partials read + out and lse written")
+            "bytes per launch: split partials (output precision) and LSEs read + out and lse written")
 
 
 class _Same:
