@@ -348,6 +348,7 @@ __global__ __launch_bounds__(QB * 64) void idx_prefill_kernel(IndexLaunch a, int
     const int kt = blockIdx.y + ksplit * j;
     if (active && kt * TK <= p) {
       const uint8_t* tile = &ring[j % kPreRing][0];
+      float mine = 0.f;                            // score of key kt*TK + lane
 #pragma unroll
       for (int st = 0; st < TK / 16; ++st) {
         const int rr = 16 * st + r16;
@@ -359,12 +360,15 @@ __global__ __launch_bounds__(QB * 64) void idx_prefill_kernel(IndexLaunch a, int
         } else {
           kf.v = join(ld16(lrow + (((2 * g) ^ (rr & 7)) * 16)), ld16(lrow + (((2 * g + 1) ^ (rr & 7)) * 16)));
         }
-        float s = tile_score<FP8>(q, kf, wv);
-        const int key = kt * TK + 16 * st + lane;
-        if (lane < 16 && key <= p) {
-          if constexpr (FP8) s *= ue8m0_to_f32(ks[key]);
-          out[key] = s;
-        }
+        // every lane holds the score of key 16 st + r16; lane 16 st + r16 keeps it
+        const float s = tile_score<FP8>(q, kf, wv);
+        mine = g == st ? s : mine;
+      }
+      // one 256-byte store per tile and wave
+      const int key = kt * TK + lane;
+      if (key <= p) {
+        if constexpr (FP8) mine *= ue8m0_to_f32(ks[key]);
+        out[key] = mine;
       }
     }
   }
