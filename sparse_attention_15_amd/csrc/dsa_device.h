@@ -79,6 +79,18 @@ __device__ __forceinline__ void xor32_pair(float x, float& a, float& b) {
   b = __builtin_bit_cast(float, v);
 }
 
+// Values of lanes l and l ^ 16 (v_permlane16_swap exchanges the odd 16-lane
+// rows of its first operand with the even rows of its second; with both
+// holding x, one ends up with rows (0, 0, 2, 2) and the other with (1, 1, 3, 3)
+// of x, so their sum is x[l] + x[l ^ 16]).  Same asm form and wait states as
+// xor32_pair.
+__device__ __forceinline__ void xor16_pair(float x, float& a, float& b) {
+  uint32_t u = __builtin_bit_cast(uint32_t, x), v = u;
+  asm volatile("s_nop 1\n\tv_permlane16_swap_b32 %0, %1" : "+v"(u), "+v"(v));
+  a = __builtin_bit_cast(float, u);
+  b = __builtin_bit_cast(float, v);
+}
+
 // s_waitcnt on the vector-memory counter only (gfx9 encoding: expcnt and
 // lgkmcnt fields left at their maxima).
 template <int N>

@@ -115,10 +115,11 @@ __device__ __forceinline__ void load_query(const IndexLaunch& a, int64_t qrow, i
     }
 }
 
-// Scores of one 16-key tile for one query: returns the score of key r in
-// every lane (all four k-groups hold the same value after the reduction).
+// This lane's part of the scores of one 16-key tile for one query: the
+// ReLU-weighted sum over its 16 heads (16m + 4g + j) for key r; the four
+// k-groups' parts add up to the score.
 template <bool FP8>
-__device__ __forceinline__ float tile_score(const QFrag<FP8>& q, const KFrag<FP8>& kf, const float (&wv)[16]) {
+__device__ __forceinline__ float tile_partial(const QFrag<FP8>& q, const KFrag<FP8>& kf, const float (&wv)[16]) {
   f32x4 acc[4];
 #pragma unroll
   for (int m = 0; m < 4; ++m) acc[m] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -137,12 +138,41 @@ __device__ __forceinline__ float tile_score(const QFrag<FP8>& q, const KFrag<FP8
   for (int m = 0; m < 4; ++m)
 #pragma unroll
     for (int j = 0; j < 4; ++j) s = fmaf(wv[4 * m + j], fmaxf(acc[m][j], 0.f), s);
-  // sum over the four 16-lane groups: a shuffle across 16 lanes, then the
-  // two halves of the wave through v_permlane32_swap
-  s += shfl_xor(s, 16);
+  return s;
+}
+
+// Scores of one 16-key tile for one query: returns the score of key r in
+// every lane (all four k-groups hold the same value after the reduction).
+template <bool FP8>
+__device__ __forceinline__ float tile_score(const QFrag<FP8>& q, const KFrag<FP8>& kf, const float (&wv)[16]) {
+  float s = tile_partial<FP8>(q, kf, wv);
+  // sum over the four 16-lane groups: rows l and l ^ 16 through
+  // v_permlane16_swap, then the two halves of the wave through
+  // v_permlane32_swap (no LDS round trips)
+  float r0, r1;
+  xor16_pair(s, r0, r1);
+  s = r0 + r1;
   float lo, hi;
   xor32_pair(s, lo, hi);
   return lo + hi;
+}
+
+// Four tiles' parts p[t] (lane group g holds group g's part of each) ->
+// lane group g returns the score of tile g: a reduce-scatter in two swaps.
+// v_permlane16_swap(a, b) leaves, in even rows, (own a, partner's a) and, in
+// odd rows, (partner's b, own b); v_permlane32_swap does the same for the
+// wave halves.  Sums come out as (g0 + g1) + (g2 + g3), as in tile_score.
+__device__ __forceinline__ float reduce4(float p0, float p1, float p2, float p3) {
+  uint32_t a0 = __builtin_bit_cast(uint32_t, p0), a1 = __builtin_bit_cast(uint32_t, p1);
+  uint32_t b0 = __builtin_bit_cast(uint32_t, p2), b1 = __builtin_bit_cast(uint32_t, p3);
+  asm volatile("s_nop 1\n\tv_permlane16_swap_b32 %0, %1\n\tv_permlane16_swap_b32 %2, %3"
+               : "+v"(a0), "+v"(a1), "+v"(b0), "+v"(b1));
+  // pair sums over rows (0, 1) and (2, 3): even rows hold tiles 0 (a) and
+  // 2 (b), odd rows tiles 1 and 3
+  uint32_t ta = __builtin_bit_cast(uint32_t, __builtin_bit_cast(float, a0) + __builtin_bit_cast(float, a1));
+  uint32_t tb = __builtin_bit_cast(uint32_t, __builtin_bit_cast(float, b0) + __builtin_bit_cast(float, b1));
+  asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1" : "+v"(ta), "+v"(tb));
+  return __builtin_bit_cast(float, ta) + __builtin_bit_cast(float, tb);
 }
 
 // ------------------------------------------------------ decode shape -------
@@ -348,7 +378,7 @@ __global__ __launch_bounds__(QB * 64) void idx_prefill_kernel(IndexLaunch a, int
     const int kt = blockIdx.y + ksplit * j;
     if (active && kt * TK <= p) {
       const uint8_t* tile = &ring[j % kPreRing][0];
-      float mine = 0.f;                            // score of key kt*TK + lane
+      float part[TK / 16];                         // this lane's parts of the 4 sub-tiles
 #pragma unroll
       for (int st = 0; st < TK / 16; ++st) {
         const int rr = 16 * st + r16;
@@ -360,10 +390,10 @@ __global__ __launch_bounds__(QB * 64) void idx_prefill_kernel(IndexLaunch a, int
         } else {
           kf.v = join(ld16(lrow + (((2 * g) ^ (rr & 7)) * 16)), ld16(lrow + (((2 * g + 1) ^ (rr & 7)) * 16)));
         }
-        // every lane holds the score of key 16 st + r16; lane 16 st + r16 keeps it
-        const float s = tile_score<FP8>(q, kf, wv);
-        mine = g == st ? s : mine;
+        part[st] = tile_partial<FP8>(q, kf, wv);
       }
+      // lane 16 g + r16 gets the score of key 16 g + r16
+      float mine = reduce4(part[0], part[1], part[2], part[3]);
       // one 256-byte store per tile and wave
       const int key = kt * TK + lane;
       if (key <= p) {
