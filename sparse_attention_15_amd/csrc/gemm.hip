@@ -13,7 +13,7 @@
 //
 // Tile kernel (more than 32 rows): 4 waves as 2 x 2, each a TM x TN block of
 // 32x32x16 MFMAs; 64-k stages (128 bytes per row) in LDS with chunk c of row r
-// stored at c ^ (r & 7), so the 32 rows of an operand read spread over the
+// stored at c ^ ((r >> 1) & 7), so the rows of an operand read spread over the
 // banks; the next stage is loaded into registers while the current one is
 // multiplied, one barrier per stage.
 // Skinny kernel (at most 32 rows, the decode shapes, which stream the
@@ -33,7 +33,12 @@ namespace {
 
 constexpr int kGK = 64;                          // k per stage: 8 chunks of 16 bytes per row
 
-__device__ __forceinline__ uint32_t tile_off(int r, int c) { return (uint32_t)(r * 128 + ((c ^ (r & 7)) << 4)); }
+// Stage rows are 128 bytes (8 chunks of 16); chunk c of row r is stored at
+// c ^ ((r >> 1) & 7).  A 16-lane group of a 16-byte operand read covers 16
+// consecutive rows, two per 256-byte bank window: rows of one parity then
+// take 8 distinct slots, so the group reads without bank conflicts.
+__device__ __forceinline__ int swz8(int r) { return (r >> 1) & 7; }
+__device__ __forceinline__ uint32_t tile_off(int r, int c) { return (uint32_t)(r * 128 + ((c ^ swz8(r)) << 4)); }
 
 __device__ __forceinline__ void store_c(const GemmLaunch& g, void* cb, int m, int n, float v) {
   if (g.c_f32)
@@ -220,6 +225,113 @@ __global__ __launch_bounds__(256) void gemm_split_reduce_kernel(GemmLaunch g) {
   store_c(g, cb, m, n, v);
 }
 
+// Big-tile kernel (many rows, k a multiple of 64): a 256 x BN output tile,
+// 4 waves as 2 x 2 of 128 x BN/2 (4 x BN/64 tiles of 32x32x16 MFMAs).  At
+// 128 x 128 tiles the L2 -> CU traffic per flop matches the chip's balance
+// point; 256 x BN halves it.  64-k stages move global -> LDS by LDS-DMA (no
+// registers), with the chunk permutation applied on the source side; NST stages in a ring, NST - 1 in flight, one barrier per stage.  The
+// output leaves through LDS, 16 bytes per lane along rows.
+template <int BN, int NST>
+__global__ __launch_bounds__(256, 1) void gemm_big_kernel(GemmLaunch g) {
+  constexpr int BM = 256, TM = 128, TN = BN / 2, IM = TM / 32, IN = TN / 32;
+  constexpr int STAGE = (BM + BN) * 128;          // bytes per stage: rows of 64 bf16
+  constexpr int NCOPY = STAGE / 1024;             // 1 KB copies per stage
+  constexpr int CPW = NCOPY / 4;                  // per wave
+  constexpr int ACOPY = BM * 128 / 1024;          // the first ACOPY copies fill A rows
+  static_assert(NCOPY % 4 == 0, "copies split evenly over the waves");
+  __shared__ __attribute__((aligned(16))) uint8_t lds[NST * STAGE];
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave >> 1, wn = wave & 1;
+  const int n0 = blockIdx.x * BN, m0 = blockIdx.y * BM;
+  const int nk = g.K / kGK;
+  // uniform bases at this tile's first rows (per-lane offsets stay small)
+  const uint8_t* abase = reinterpret_cast<const uint8_t*>(g.A + (int64_t)blockIdx.z * g.sa + (int64_t)m0 * g.lda);
+  const uint8_t* bbase = reinterpret_cast<const uint8_t*>(g.B + (int64_t)blockIdx.z * g.sb + (int64_t)n0 * g.ldb);
+  // copy c = wave * CPW + k (uniform) fills A rows if c < ACOPY, else B rows
+  uint32_t off[CPW];
+#pragma unroll
+  for (int k = 0; k < CPW; ++k) {
+    const int f = 64 * (wave * CPW + k) + lane;   // LDS slot of the stage
+    const int r = f >> 3, c = (f & 7) ^ swz8(r);  // row, global chunk stored there
+    if (wave * CPW + k < ACOPY) off[k] = (uint32_t)((min(m0 + r, g.M - 1) - m0) * g.lda * 2 + 16 * c);
+    else off[k] = (uint32_t)((min(n0 + r - BM, g.N - 1) - n0) * g.ldb * 2 + 16 * c);
+  }
+  const uint32_t lds0 = lds_addr(lds);
+  auto issue = [&](int st) {
+    const uint32_t dst = __builtin_amdgcn_readfirstlane(lds0 + (st % NST) * STAGE + 1024 * wave * CPW);
+#pragma unroll
+    for (int k = 0; k < CPW; ++k) {
+      const uint8_t* gb = (wave * CPW + k < ACOPY ? abase : bbase) + (int64_t)st * (kGK * 2);
+      lds_dma16<false>(gb, off[k], dst + 1024 * k);
+    }
+  };
+
+  f32x16 acc[IM][IN];
+#pragma unroll
+  for (int i = 0; i < IM; ++i)
+#pragma unroll
+    for (int j = 0; j < IN; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
+
+  const int half = lane >> 5, r32 = lane & 31;
+#pragma unroll
+  for (int j = 0; j < NST - 1; ++j)
+    if (j < nk) issue(j);
+  for (int st = 0; st < nk; ++st) {
+    // this wave's copies of stage st landed once at most the later issued
+    // stages' copies are outstanding
+    const int ahead = min(nk - 1 - st, NST - 2);
+    if (ahead >= 2) wait_vmcnt<2 * CPW>();
+    else if (ahead == 1) wait_vmcnt<CPW>();
+    else wait_vmcnt<0>();
+    __syncthreads();                              // everyone's; stage st-1 is no longer read
+    if (st + NST - 1 < nk) issue(st + NST - 1);  // into the buffer of stage st-1
+    const uint8_t* base = lds + (st % NST) * STAGE;
+#pragma unroll
+    for (int s = 0; s < kGK / 16; ++s) {
+      const int kc = 2 * s + half;
+      u32x4 av[IM], bv[IN];
+#pragma unroll
+      for (int i = 0; i < IM; ++i) av[i] = ld16(base + tile_off(wm * TM + 32 * i + r32, kc));
+#pragma unroll
+      for (int j = 0; j < IN; ++j) bv[j] = ld16(base + BM * 128 + tile_off(wn * TN + 32 * j + r32, kc));
+#pragma unroll
+      for (int i = 0; i < IM; ++i)
+#pragma unroll
+        for (int j = 0; j < IN; ++j) acc[i][j] = mfma32(av[i], bv[j], acc[i][j]);
+    }
+  }
+
+  // epilogue: per 32-row slice of the wave tile, rows of TN values through a
+  // private LDS area, then 16-byte stores along the rows
+  __syncthreads();                                // the stages are free
+  const int esz = g.c_f32 ? 4 : 2;
+  const int pitch = TN * 4 + 16;                  // bytes per staged row (fp32 room, padded)
+  uint8_t* ebuf = lds + wave * 32 * pitch;
+  uint8_t* cb = static_cast<uint8_t*>(g.C) + ((int64_t)blockIdx.z * g.sc) * esz;
+  const int row_bytes = TN * esz, chunks = 32 * row_bytes / 16;
+#pragma unroll
+  for (int i = 0; i < IM; ++i) {
+#pragma unroll
+    for (int j = 0; j < IN; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int rr = 8 * (e >> 2) + 4 * half + (e & 3), cc = 32 * j + r32;
+        if (g.c_f32) *reinterpret_cast<float*>(ebuf + rr * pitch + cc * 4) = acc[i][j][e];
+        else *reinterpret_cast<uint16_t*>(ebuf + rr * pitch + cc * 2) = f32_to_bf16_bits(acc[i][j][e]);
+      }
+    __builtin_amdgcn_s_waitcnt(0xc07f);           // lgkmcnt(0): this wave's LDS writes are done
+    for (int q = lane; q < chunks; q += 64) {
+      const int rr = q / (row_bytes / 16), cq = q - rr * (row_bytes / 16);
+      const int m = m0 + wm * TM + 32 * i + rr;
+      const int n = n0 + wn * TN + cq * (16 / esz);
+      if (m < g.M && n < g.N) st16(cb + ((int64_t)m * g.ldc + n) * esz, ld16(ebuf + rr * pitch + cq * 16));
+    }
+    __builtin_amdgcn_s_waitcnt(0xc07f);           // reads done before the next slice overwrites
+  }
+}
+
 }  // namespace
 
 int gemm_ksplit(int M, int N, int K, int batch, size_t* bytes) {
@@ -255,6 +367,10 @@ hipError_t launch_gemm_bt(const GemmLaunch& g, hipStream_t s) {
       hipLaunchKernelGGL(gemm_skinny_kernel<8>, grid, dim3(512), 0, s, g);
     else
       hipLaunchKernelGGL(gemm_skinny_kernel<16>, grid, dim3(1024), 0, s, g);
+  } else if (g.M >= 256 && g.N >= 128 && g.K % kGK == 0 && g.N % 8 == 0 && g.ldc % 8 == 0 &&
+             (g.sc * (g.c_f32 ? 4 : 2)) % 16 == 0 && (reinterpret_cast<uintptr_t>(g.C) & 15) == 0) {
+    dim3 grid((g.N + 127) / 128, (g.M + 255) / 256, g.batch);
+    hipLaunchKernelGGL((gemm_big_kernel<128, 3>), grid, dim3(256), 0, s, g);
   } else if (g.M >= 128 && g.N >= 128) {
     dim3 grid((g.N + 127) / 128, (g.M + 127) / 128, g.batch);
     hipLaunchKernelGGL((gemm_tile_kernel<64, 64>), grid, dim3(256), 0, s, g);

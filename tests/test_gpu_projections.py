@@ -52,6 +52,10 @@ SMALL = [
     ("200_tokens", C.scaled(C.DECODE_32K, batch=2, q_len=100, kv_len=100), 1536, 7168, 128),
     ("ragged_small", C.scaled(C.TINY, batch=2, q_len=37, kv_len=37, index_heads=3, index_dim=8, attn_heads=5,
                               v_dim=40, qk_dim=48), 24, 88, 24),
+    # 300 tokens: the 256-row tile kernels with a ragged row tile; N = 384
+    # (256-wide tiles, ragged) and 136 (128-wide tiles, ragged)
+    ("ragged_big", C.scaled(C.TINY, batch=3, q_len=100, kv_len=100, index_heads=24, index_dim=16, attn_heads=6,
+                            v_dim=512, qk_dim=576), 1536, 7168, 136),
 ]
 
 
