@@ -290,6 +290,40 @@ def test_forward_edge_shapes(case):
     _check_forward(cfg, inp, host, out, idx, lse, label=str(case))
 
 
+@pytest.mark.parametrize("case", [
+    # K > 4096: top-k emits straight to memory, attention windows span several
+    # 2048-entry windows (more splits)
+    dict(name="k5000_decode", batch=2, q_len=1, kv_len=9000, topk=5000),
+    dict(name="k5000_prefill", batch=1, q_len=6, kv_len=7000, topk=5000),
+    # two-stage top-k (>= 65536 positions) with spare cache capacity
+    dict(name="two_stage_capacity", batch=2, q_len=1, kv_len=70001, capacity=70100),
+    # FP8 index at 128K context: FP8 scores, two-stage top-k, 32 splits
+    dict(name="fp8_128k", batch=1, q_len=1, kv_len=131072, fp8=True),
+])
+def test_forward_wide_cases(case):
+    dsa = _dsa()
+    case = dict(case)
+    name, cap, fp8 = case.pop("name"), case.pop("capacity", 0), case.pop("fp8", False)
+    base = C.PREFILL_64K_FP8 if fp8 else C.DECODE_32K
+    cfg = C.scaled(base, name=name, plant_count=0 if fp8 else 40, **case)
+    inp, host = _inputs(cfg)
+    p = dsa.make_problem(cfg, kv_capacity=cap)
+    args = dict(inp)
+    if cap:
+        # caches with room for more tokens than the context
+        for key, tail in (("k_idx", (cfg.index_dim,)), ("kv", (cfg.qk_dim,))):
+            t = torch.zeros((cfg.batch, cap) + tail, dtype=inp[key].dtype, device=DEV)
+            t[:, :cfg.kv_len] = inp[key]
+            args[key] = t
+    lse = torch.empty(cfg.batch, cfg.q_len, cfg.attn_heads, dtype=torch.float32, device=DEV)
+    idx = torch.empty(cfg.batch, cfg.q_len, cfg.topk, dtype=torch.int32, device=DEV)
+    out, lse, idx = dsa.forward(p, args["q_idx"], args["q_scale"], args["k_idx"], args["k_scale"], args["head_w"],
+                                args["q_attn"], args["kv"], lse=lse, topk_idx=idx)
+    torch.cuda.synchronize()
+    rows = [(b, i) for b in range(cfg.batch) for i in sorted({0, cfg.q_len - 1})]
+    _check_forward(cfg, inp, host, out, idx, lse, rows=rows, label=name)
+
+
 # ------------------------------------------------------------ full size ----
 def _sample_rows(cfg, k):
     rows = []
