@@ -26,6 +26,8 @@
 // x its slot is  #(key > T before x) + min(#(key == T before x), r), from
 // block-wide scans of packed counts (one barrier per group of 8 chunks).
 // Slots go to LDS first and leave in one coalesced copy (K <= 4096).
+#include <type_traits>
+
 #include "dsa_device.h"
 #include "dsa_internal.h"
 
@@ -37,10 +39,15 @@ constexpr int kWaves = kThreads / 64;
 constexpr int kBins = 4096;
 constexpr int kGroup = 8;            // chunks per emission group
 
+// Key 0 is reserved for positions that hold no element (the tail of the
+// last 16-byte chunk, unused candidate slots); real elements map to >= 1
+// (only the all-ones NaN pattern would map to 0, and NaN scores have no
+// defined place in the order).
 __device__ __forceinline__ uint32_t order_key(float x) {
   uint32_t u = __builtin_bit_cast(uint32_t, x);
   if (u == 0x80000000u) u = 0u;                 // -0.0 == +0.0
-  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  const uint32_t k = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  return k > 1u ? k : 1u;
 }
 
 // DPP source shift (lanes whose source is out of range read 0).
@@ -70,18 +77,32 @@ struct Shared {
   alignas(16) uint32_t hist[C * kStride];   // histograms; at the end the output stage
   uint32_t gt_bits[kWords];         // position x: bit x % 32 of word x / 32
   uint32_t eq_bits[kWords];
-  uint32_t wsum[kGroup * kWaves];
+  alignas(16) uint32_t wsum[kGroup * kWaves];
   uint32_t bin;                     // chosen bin of the current pass
   uint32_t above;                   // elements in bins above it
   uint32_t cnt;                     // elements in it
 };
 
+// Sum of the per-wave totals ws[0..kWaves) over the waves before `wave`:
+// lane l of each 16-lane row reads total l (or 0), a row scan leaves the sum
+// in lane 15, read out as a uniform value.
+__device__ __forceinline__ uint32_t sum_before(const uint32_t* ws, int wave) {
+  static_assert(kWaves == 16, "one total per lane of a 16-lane row");
+  const int l = threadIdx.x & 15;
+  uint32_t v = l < wave ? ws[l] : 0u;
+  v += dpp<0x111, 0xf>(v);
+  v += dpp<0x112, 0xf>(v);
+  v += dpp<0x114, 0xf>(v);
+  v += dpp<0x118, 0xf>(v);
+  return (uint32_t)__builtin_amdgcn_readlane((int)v, 15);
+}
+
 // Find the bin holding the k-th largest element (k >= 1) of a histogram of
-// nb bins (4096 or 256).  Thread t owns a run of bins counted from the top,
-// so a block-wide scan of the per-thread sums gives each run the number of
-// elements above it.  Returns via sh.bin / sh.above / sh.cnt.  All threads
-// must call.
-template <int NC, int C>
+// nb bins (4096 or 256) kept in NCOPY copies.  Thread t owns a run of bins
+// counted from the top, so a block-wide scan of the per-thread sums gives
+// each run the number of elements above it.  Returns via sh.bin / sh.above /
+// sh.cnt.  All threads must call.
+template <int NCOPY, int NC, int C>
 __device__ void find_bin(Shared<NC, C>& sh, int nb, uint32_t k) {
   constexpr int S = Shared<NC, C>::kStride;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -92,7 +113,7 @@ __device__ void find_bin(Shared<NC, C>& sh, int nb, uint32_t k) {
     per = 4;
     top = nb - 1 - 4 * tid;
 #pragma unroll
-    for (int r = 0; r < C; ++r) {
+    for (int r = 0; r < NCOPY; ++r) {
       const u32x4 v = *reinterpret_cast<const u32x4*>(&sh.hist[r * S + top - 3]);
       c4[0] += v.w;
       c4[1] += v.z;
@@ -104,15 +125,13 @@ __device__ void find_bin(Shared<NC, C>& sh, int nb, uint32_t k) {
     top = nb - 1 - tid;
     if (top >= 0)
 #pragma unroll
-      for (int r = 0; r < C; ++r) c4[0] += sh.hist[r * S + top];
+      for (int r = 0; r < NCOPY; ++r) c4[0] += sh.hist[r * S + top];
   }
   const uint32_t local = c4[0] + c4[1] + c4[2] + c4[3];
   const uint32_t incl = wave_incl_scan(local);
   if (lane == 63) sh.wsum[wave] = incl;
   __syncthreads();
-  uint32_t before = 0;
-  for (int w = 0; w < wave; ++w) before += sh.wsum[w];
-  uint32_t run = before + incl - local;          // count strictly above my bins
+  uint32_t run = sum_before(sh.wsum, wave) + incl - local;   // count strictly above my bins
   if (run < k && run + local >= k) {
     for (int j = 0; j < per; ++j) {
       if (run + c4[j] >= k) {
@@ -136,7 +155,7 @@ enum { kRows = 0, kSlice = 1, kCand = 2 };
 // NC 16-byte chunks per thread kept in registers (0 = re-read each pass);
 // C histogram copies.
 template <int NC, int C, int MODE>
-__global__ __launch_bounds__(kThreads) void topk_kernel(TopkLaunch a) {
+__global__ __launch_bounds__(kThreads, NC == 2 ? 8 : 4) void topk_kernel(TopkLaunch a) {
   __shared__ Shared<NC, C> sh;
   constexpr int S = Shared<NC, C>::kStride;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -222,24 +241,41 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(TopkLaunch a) {
   }
 
   // Radix passes.  prefix/mask describe the candidate set; k_rem counts how
-  // many candidates are still to be taken (>= 1).
+  // many candidates are still to be taken (>= 1).  The first pass spreads
+  // its atomics over C histogram copies; later passes only count the
+  // elements of one bin, which the next 12 (8) bits spread thinly, so they
+  // use one copy (a quarter to an eighth of the clearing and reading).
   uint32_t prefix = 0, mask = 0, k_rem = (uint32_t)K;
-  const int shifts[3] = {20, 8, 0};
-  const int widths[3] = {12, 12, 8};
+  bool whole = false;                             // the last bin is taken whole
   const uint32_t copy_base = (uint32_t)(lane & (C - 1)) * S;
+  // Loaded slots past the row's end hold key 0.  Rows (not candidate lists)
+  // know how many there are: the first pass counts every slot, the padding
+  // into bin 0, and takes that many out of bin 0 again (atomics commute).
+  const uint32_t pad = (uint32_t)(iters * kThreads * 4 - n);
+#pragma unroll
   for (int pass = 0; pass < 3; ++pass) {
-    const int sh_ = shifts[pass], nb = 1 << widths[pass];
-    for (int j = tid; j < C * nb / 4; j += kThreads) {
+    const int sh_ = pass == 0 ? 20 : (pass == 1 ? 8 : 0);
+    const int nb = pass == 2 ? 256 : 4096;
+    const int ncopy = pass == 0 ? C : 1;
+    for (int j = tid; j < ncopy * nb / 4; j += kThreads) {
       const int r = j / (nb / 4), o = j - r * (nb / 4);
       st16(&sh.hist[r * S + 4 * o], u32x4{0u, 0u, 0u, 0u});
     }
     __syncthreads();
+    const bool every = pass == 0 && MODE != kCand;
+    // after the first pass prefix != 0 unless bin 0 was chosen; only then
+    // can a padding key (0) match the prefix
+    const bool check_pad = prefix == 0u;
     auto count = [&](const uint32_t (&kk)[4]) {
 #pragma unroll
-      for (int e = 0; e < 4; ++e)
-        if ((kk[e] & mask) == prefix && kk[e] != 0u)
-          atomicAdd(&sh.hist[copy_base + ((kk[e] >> sh_) & (nb - 1))], 1u);
+      for (int e = 0; e < 4; ++e) {
+        if (every)
+          atomicAdd(&sh.hist[copy_base + (kk[e] >> 20)], 1u);
+        else if ((kk[e] & mask) == prefix && (!check_pad || kk[e] != 0u))
+          atomicAdd(&sh.hist[(pass == 0 ? copy_base : 0u) + ((kk[e] >> sh_) & (nb - 1))], 1u);
+      }
     };
+    if (every && tid == 0 && pad != 0u) atomicSub(&sh.hist[0], pad);
     if constexpr (NC > 0) {
 #pragma unroll
       for (int c = 0; c < NC; ++c)
@@ -252,13 +288,19 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(TopkLaunch a) {
       }
     }
     __syncthreads();
-    find_bin(sh, nb, k_rem);
+    if (pass == 0)
+      find_bin<C>(sh, nb, k_rem);
+    else
+      find_bin<1>(sh, nb, k_rem);
     const uint32_t bin = sh.bin;
     const uint32_t cnt = sh.cnt;
     k_rem -= sh.above;
     prefix |= bin << sh_;
     mask |= (uint32_t)(nb - 1) << sh_;
-    if (cnt == k_rem) break;                      // the whole bin is taken
+    if (cnt == k_rem) {                           // the whole bin is taken
+      whole = true;
+      break;
+    }
   }
   // hist is free from here on (the last find_bin ended with a barrier and
   // nothing reads it after): it becomes the output stage.
@@ -273,80 +315,98 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(TopkLaunch a) {
   if constexpr (NC > 0) {
     // Bitmaps: chunk c of thread t covers positions 4*(c*kThreads + t) + e,
     // so the 8 lanes t = 8m..8m+7 fill word c*kThreads/8 + m, 4 bits each.
-    const int sub = lane & 7;
+    // WHOLE: the last bin was taken whole, so the selection is simply
+    // key >= prefix (prefix != 0 excludes padding) and one bitmap suffices.
+    auto emit_bits = [&](auto whole_tag) {
+      constexpr bool WHOLE = decltype(whole_tag)::value;
+      const int sub = lane & 7;
 #pragma unroll
-    for (int c = 0; c < NC; ++c) {
-      uint32_t gn = 0u, en = 0u;
+      for (int c = 0; c < NC; ++c) {
+        uint32_t gn = 0u, en = 0u;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const uint32_t k = keys[c][e], m = k & mask;
-        const bool valid = k != 0u;
-        gn |= (valid && m > prefix) ? (1u << e) : 0u;
-        en |= (valid && m == prefix) ? (1u << e) : 0u;
-      }
-      // OR over lanes l-7..l: complete at lanes 7 and 15 of each DPP row
-      uint32_t gw = gn << (4 * sub), ew = en << (4 * sub);
-      gw |= dpp<0x111, 0xf>(gw);
-      ew |= dpp<0x111, 0xf>(ew);
-      gw |= dpp<0x112, 0xf>(gw);
-      ew |= dpp<0x112, 0xf>(ew);
-      gw |= dpp<0x114, 0xf>(gw);
-      ew |= dpp<0x114, 0xf>(ew);
-      if (sub == 7) {
-        sh.gt_bits[c * (kThreads / 8) + (tid >> 3)] = gw;
-        sh.eq_bits[c * (kThreads / 8) + (tid >> 3)] = ew;
-      }
-    }
-    __syncthreads();
-    // One thread per J consecutive words, in position order.
-    constexpr int W = Shared<NC, C>::kWords;
-    constexpr int J = W >= kThreads ? W / kThreads : 1;
-    const bool act = tid * J < W;
-    uint32_t gw[J], ew[J], gc = 0u, ec = 0u;
-#pragma unroll
-    for (int j = 0; j < J; ++j) {
-      gw[j] = act ? sh.gt_bits[tid * J + j] : 0u;
-      ew[j] = act ? sh.eq_bits[tid * J + j] : 0u;
-      gc += __builtin_popcount(gw[j]);
-      ec += __builtin_popcount(ew[j]);
-    }
-    const uint32_t gi = wave_incl_scan(gc), ei = wave_incl_scan(ec);
-    if (lane == 63) {
-      sh.wsum[wave] = gi;
-      sh.wsum[kWaves + wave] = ei;
-    }
-    __syncthreads();
-    uint32_t g_b = gi - gc, e_b = ei - ec;        // counts before my first word
-    for (int w = 0; w < wave; ++w) {
-      g_b += sh.wsum[w];
-      e_b += sh.wsum[kWaves + w];
-    }
-#pragma unroll
-    for (int j = 0; j < J; ++j) {
-      // equal positions are taken while fewer than k_rem came before
-      uint32_t ek = ew[j];
-      if (e_b >= k_rem) {
-        ek = 0u;
-      } else if (e_b + __builtin_popcount(ek) > k_rem) {
-        uint32_t keep = 0u, rest = ek;
-        for (uint32_t q = k_rem - e_b; q > 0u; --q) {
-          const uint32_t low = rest & (0u - rest);
-          keep |= low;
-          rest ^= low;
+        for (int e = 0; e < 4; ++e) {
+          const uint32_t k = keys[c][e];
+          if constexpr (WHOLE) {
+            gn |= k >= prefix ? (1u << e) : 0u;
+          } else {
+            const uint32_t m = k & mask;
+            const bool valid = k != 0u;
+            gn |= (valid && m > prefix) ? (1u << e) : 0u;
+            en |= (valid && m == prefix) ? (1u << e) : 0u;
+          }
         }
-        ek = keep;
+        // OR over lanes l-7..l: complete at lanes 7 and 15 of each DPP row
+        uint32_t gw = gn << (4 * sub);
+        gw |= dpp<0x111, 0xf>(gw);
+        gw |= dpp<0x112, 0xf>(gw);
+        gw |= dpp<0x114, 0xf>(gw);
+        if (sub == 7) sh.gt_bits[c * (kThreads / 8) + (tid >> 3)] = gw;
+        if constexpr (!WHOLE) {
+          uint32_t ew = en << (4 * sub);
+          ew |= dpp<0x111, 0xf>(ew);
+          ew |= dpp<0x112, 0xf>(ew);
+          ew |= dpp<0x114, 0xf>(ew);
+          if (sub == 7) sh.eq_bits[c * (kThreads / 8) + (tid >> 3)] = ew;
+        }
       }
-      uint32_t sel = gw[j] | ek;
-      uint32_t slot = g_b + min(e_b, k_rem);
-      const int base = 32 * (tid * J + j);
-      while (sel != 0u) {
-        put(slot++, pos_of(base + __builtin_ctz(sel)));
-        sel &= sel - 1u;
+      __syncthreads();
+      // One thread per J consecutive words, in position order.
+      constexpr int W = Shared<NC, C>::kWords;
+      constexpr int J = W >= kThreads ? W / kThreads : 1;
+      const bool act = tid * J < W;
+      uint32_t gw[J], ew[J], gc = 0u, ec = 0u;
+#pragma unroll
+      for (int j = 0; j < J; ++j) {
+        gw[j] = act ? sh.gt_bits[tid * J + j] : 0u;
+        ew[j] = (!WHOLE && act) ? sh.eq_bits[tid * J + j] : 0u;
+        gc += __builtin_popcount(gw[j]);
+        if constexpr (!WHOLE) ec += __builtin_popcount(ew[j]);
       }
-      g_b += __builtin_popcount(gw[j]);
-      e_b += __builtin_popcount(ew[j]);
-    }
-    __syncthreads();                              // the stage is complete
+      const uint32_t gi = wave_incl_scan(gc);
+      const uint32_t ei = WHOLE ? 0u : wave_incl_scan(ec);
+      if (lane == 63) {
+        sh.wsum[wave] = gi;
+        if constexpr (!WHOLE) sh.wsum[kWaves + wave] = ei;
+      }
+      __syncthreads();
+      // counts before my first word
+      uint32_t g_b = gi - gc + sum_before(sh.wsum, wave);
+      uint32_t e_b = WHOLE ? 0u : ei - ec + sum_before(sh.wsum + kWaves, wave);
+#pragma unroll
+      for (int j = 0; j < J; ++j) {
+        uint32_t sel = gw[j];
+        uint32_t slot = g_b;
+        if constexpr (!WHOLE) {
+          // equal positions are taken while fewer than k_rem came before
+          uint32_t ek = ew[j];
+          if (e_b >= k_rem) {
+            ek = 0u;
+          } else if (e_b + __builtin_popcount(ek) > k_rem) {
+            uint32_t keep = 0u, rest = ek;
+            for (uint32_t q = k_rem - e_b; q > 0u; --q) {
+              const uint32_t low = rest & (0u - rest);
+              keep |= low;
+              rest ^= low;
+            }
+            ek = keep;
+          }
+          sel |= ek;
+          slot += min(e_b, k_rem);
+        }
+        const int base = 32 * (tid * J + j);
+        while (sel != 0u) {
+          put(slot++, pos_of(base + __builtin_ctz(sel)));
+          sel &= sel - 1u;
+        }
+        g_b += __builtin_popcount(gw[j]);
+        if constexpr (!WHOLE) e_b += __builtin_popcount(ew[j]);
+      }
+      __syncthreads();                            // the stage is complete
+    };
+    if (whole && prefix != 0u)
+      emit_bits(std::true_type{});
+    else
+      emit_bits(std::false_type{});
   } else {
     // Ordered emission: chunk c holds positions 4*(c*kThreads + tid) + 0..3,
     // so positions run over (chunk, thread, element).  A group of chunks is
