@@ -233,10 +233,86 @@ __global__ __launch_bounds__(kThreads, NC == 2 ? 8 : 4) void topk_kernel(TopkLau
 
   uint32_t keys[NC > 0 ? NC : 1][4];
   if constexpr (NC > 0) {
+    // Every load of the row is issued before any is converted, so the
+    // chunks' latencies overlap and each conversion waits only for its own
+    // chunk.  Chunks whole for every lane take one 16-byte load each, issued
+    // unconditionally (chunks past the row re-read its first 16 bytes and
+    // are masked): loads inside lane- or value-dependent branches would make
+    // each chunk wait for the one before.  The ragged chunk (positions past
+    // n read nothing) is loaded first, into registers of its own.
+    const int cfull = a.vec_ok ? n / (4 * kThreads) : 0;
+    const int crag = cfull < iters ? cfull : NC;  // the chunk loaded lane by lane
+    auto inside = [&](int c, int e) { return c < cfull || (c < iters && (c * kThreads + tid) * 4 + e < n); };
+    if (a.vec_ok && NC >= 8 && (MODE != kCand || NC <= 8)) {
+      float vr[4] = {0.f, 0.f, 0.f, 0.f};        // the ragged chunk
+      int32_t ar[4] = {-1, -1, -1, -1};
+      const int rpos = (crag * kThreads + tid) * 4;
+      if (crag < NC) {                            // lanes wholly inside still take one load
+        if constexpr (MODE == kCand) {
+          if (rpos + 3 < n) {
+            const u32x4 cv = ld16(cand + rpos);
 #pragma unroll
-    for (int c = 0; c < NC; ++c) {
-      if (c < iters) load_keys(c, keys[c]);
-      else keys[c][0] = keys[c][1] = keys[c][2] = keys[c][3] = 0u;
+            for (int e = 0; e < 4; ++e) ar[e] = (int32_t)cv[e];
+          } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) ar[e] = rpos + e < n ? cand[rpos + e] : -1;
+          }
+        } else {
+          if (rpos + 3 < n) {
+            const f32x4 t = *reinterpret_cast<const f32x4*>(src + rpos);
+            vr[0] = t.x;
+            vr[1] = t.y;
+            vr[2] = t.z;
+            vr[3] = t.w;
+          } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) vr[e] = rpos + e < n ? src[rpos + e] : 0.f;
+          }
+        }
+      }
+      float v[NC][4];
+      if constexpr (MODE == kCand) {
+        int32_t at[NC][4];
+#pragma unroll
+        for (int c = 0; c < NC; ++c) {
+          const u32x4 cv = ld16(cand + (c < cfull ? (c * kThreads + tid) * 4 : 0));
+#pragma unroll
+          for (int e = 0; e < 4; ++e) at[c][e] = c < cfull ? (int32_t)cv[e] : (c == crag ? ar[e] : -1);
+        }
+        // gathers (unused slots read position 0)
+#pragma unroll
+        for (int c = 0; c < NC; ++c)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) v[c][e] = src[max(at[c][e], 0)];
+#pragma unroll
+        for (int c = 0; c < NC; ++c)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) keys[c][e] = at[c][e] >= 0 ? order_key(v[c][e]) : 0u;
+      } else {
+#pragma unroll
+        for (int c = 0; c < NC; ++c) {
+          const f32x4 t = *reinterpret_cast<const f32x4*>(src + (c < cfull ? (c * kThreads + tid) * 4 : 0));
+          v[c][0] = t.x;
+          v[c][1] = t.y;
+          v[c][2] = t.z;
+          v[c][3] = t.w;
+        }
+#pragma unroll
+        for (int c = 0; c < NC; ++c)
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            keys[c][e] = inside(c, e) ? order_key(c < cfull ? v[c][e] : vr[e]) : 0u;
+      }
+    } else {
+      // unaligned rows, short rows (one or two chunks: nothing to overlap,
+      // and masked extra loads cost more than they hide), and the widest
+      // candidate lists (their gathers would not fit the registers at
+      // once): chunk by chunk
+#pragma unroll
+      for (int c = 0; c < NC; ++c) {
+        if (c < iters) load_keys(c, keys[c]);
+        else keys[c][0] = keys[c][1] = keys[c][2] = keys[c][3] = 0u;
+      }
     }
   }
 
