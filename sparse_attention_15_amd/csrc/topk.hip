@@ -74,7 +74,9 @@ template <int NC, int C>
 struct Shared {
   static constexpr int kStride = kBins + 4;   // bin j, copy c at c * kStride + j
   static constexpr int kWords = NC > 0 ? NC * kThreads * 4 / 32 : 1;   // bitmap words
-  alignas(16) uint32_t hist[C * kStride];   // histograms; at the end the output stage
+  // pass 1: C copies; then copy 0 holds pass 2; at the end the output stage
+  alignas(16) uint32_t hist[C * kStride];
+  alignas(16) uint32_t h3[256];     // pass 3
   uint32_t gt_bits[kWords];         // position x: bit x % 32 of word x / 32
   uint32_t eq_bits[kWords];
   alignas(16) uint32_t wsum[kGroup * kWaves];
@@ -98,12 +100,13 @@ __device__ __forceinline__ uint32_t sum_before(const uint32_t* ws, int wave) {
 }
 
 // Find the bin holding the k-th largest element (k >= 1) of a histogram of
-// nb bins (4096 or 256) kept in NCOPY copies.  Thread t owns a run of bins
-// counted from the top, so a block-wide scan of the per-thread sums gives
-// each run the number of elements above it.  Returns via sh.bin / sh.above /
-// sh.cnt.  All threads must call.
-template <int NCOPY, int NC, int C>
-__device__ void find_bin(Shared<NC, C>& sh, int nb, uint32_t k) {
+// nb bins (4096 or 256) kept in NCOPY copies from h (stride kStride).
+// Thread t owns a run of bins counted from the top, so a block-wide scan of
+// the per-thread sums gives each run the number of elements above it.
+// Returns via sh.bin / sh.above / sh.cnt.  CLEAR: once every copy has been
+// read, zero copy 0 of sh.hist for the next pass.  All threads must call.
+template <int NCOPY, bool CLEAR, int NC, int C>
+__device__ void find_bin(Shared<NC, C>& sh, const uint32_t* h, int nb, uint32_t k) {
   constexpr int S = Shared<NC, C>::kStride;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   uint32_t c4[4] = {0u, 0u, 0u, 0u};             // my bins, highest first
@@ -114,7 +117,7 @@ __device__ void find_bin(Shared<NC, C>& sh, int nb, uint32_t k) {
     top = nb - 1 - 4 * tid;
 #pragma unroll
     for (int r = 0; r < NCOPY; ++r) {
-      const u32x4 v = *reinterpret_cast<const u32x4*>(&sh.hist[r * S + top - 3]);
+      const u32x4 v = *reinterpret_cast<const u32x4*>(&h[r * S + top - 3]);
       c4[0] += v.w;
       c4[1] += v.z;
       c4[2] += v.y;
@@ -125,12 +128,15 @@ __device__ void find_bin(Shared<NC, C>& sh, int nb, uint32_t k) {
     top = nb - 1 - tid;
     if (top >= 0)
 #pragma unroll
-      for (int r = 0; r < NCOPY; ++r) c4[0] += sh.hist[r * S + top];
+      for (int r = 0; r < NCOPY; ++r) c4[0] += h[r * S + top];
   }
   const uint32_t local = c4[0] + c4[1] + c4[2] + c4[3];
   const uint32_t incl = wave_incl_scan(local);
   if (lane == 63) sh.wsum[wave] = incl;
   __syncthreads();
+  if constexpr (CLEAR) {
+    for (int j = tid; j < kBins / 4; j += kThreads) st16(&sh.hist[4 * j], u32x4{0u, 0u, 0u, 0u});
+  }
   uint32_t run = sum_before(sh.wsum, wave) + incl - local;   // count strictly above my bins
   if (run < k && run + local >= k) {
     for (int j = 0; j < per; ++j) {
@@ -317,65 +323,87 @@ __global__ __launch_bounds__(kThreads, NC == 2 ? 8 : 4) void topk_kernel(TopkLau
   }
 
   // Radix passes.  prefix/mask describe the candidate set; k_rem counts how
-  // many candidates are still to be taken (>= 1).  The first pass spreads
-  // its atomics over C histogram copies; later passes only count the
-  // elements of one bin, which the next 12 (8) bits spread thinly, so they
-  // use one copy (a quarter to an eighth of the clearing and reading).
+  // many candidates are still to be taken (>= 1).
+  //  - Pass 1 (bits 31..20) spreads its atomics over C histogram copies.
+  //    Loaded slots past the row's end hold key 0; rows (not candidate
+  //    lists) know how many there are, so pass 1 counts every slot, the
+  //    padding into bin 0, and takes that many out of bin 0 again (atomics
+  //    commute).
+  //  - Later passes count one bin's elements, which the next bits spread
+  //    thinly: one copy.  Pass 1's find step clears copy 0 for pass 2 once
+  //    the copies are read, and pass 3 (bits 7..0) has a small histogram
+  //    cleared at the start, so no pass has a clearing step of its own.
   uint32_t prefix = 0, mask = 0, k_rem = (uint32_t)K;
   bool whole = false;                             // the last bin is taken whole
   const uint32_t copy_base = (uint32_t)(lane & (C - 1)) * S;
-  // Loaded slots past the row's end hold key 0.  Rows (not candidate lists)
-  // know how many there are: the first pass counts every slot, the padding
-  // into bin 0, and takes that many out of bin 0 again (atomics commute).
   const uint32_t pad = (uint32_t)(iters * kThreads * 4 - n);
+  for (int j = tid; j < C * kBins / 4; j += kThreads) {
+    const int r = j / (kBins / 4), o = j - r * (kBins / 4);
+    st16(&sh.hist[r * S + 4 * o], u32x4{0u, 0u, 0u, 0u});
+  }
+  if (tid < 64) st16(&sh.h3[4 * tid], u32x4{0u, 0u, 0u, 0u});
+  __syncthreads();
+  {
+    constexpr bool kEvery = MODE != kCand;
+    auto count1 = [&](const uint32_t (&kk)[4]) {
 #pragma unroll
-  for (int pass = 0; pass < 3; ++pass) {
-    const int sh_ = pass == 0 ? 20 : (pass == 1 ? 8 : 0);
-    const int nb = pass == 2 ? 256 : 4096;
-    const int ncopy = pass == 0 ? C : 1;
-    for (int j = tid; j < ncopy * nb / 4; j += kThreads) {
-      const int r = j / (nb / 4), o = j - r * (nb / 4);
-      st16(&sh.hist[r * S + 4 * o], u32x4{0u, 0u, 0u, 0u});
-    }
-    __syncthreads();
-    const bool every = pass == 0 && MODE != kCand;
-    // after the first pass prefix != 0 unless bin 0 was chosen; only then
-    // can a padding key (0) match the prefix
-    const bool check_pad = prefix == 0u;
-    auto count = [&](const uint32_t (&kk)[4]) {
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        if (every)
-          atomicAdd(&sh.hist[copy_base + (kk[e] >> 20)], 1u);
-        else if ((kk[e] & mask) == prefix && (!check_pad || kk[e] != 0u))
-          atomicAdd(&sh.hist[(pass == 0 ? copy_base : 0u) + ((kk[e] >> sh_) & (nb - 1))], 1u);
-      }
+      for (int e = 0; e < 4; ++e)
+        if (kEvery || kk[e] != 0u) atomicAdd(&sh.hist[copy_base + (kk[e] >> 20)], 1u);
     };
-    if (every && tid == 0 && pad != 0u) atomicSub(&sh.hist[0], pad);
+    if (kEvery && tid == 0 && pad != 0u) atomicSub(&sh.hist[0], pad);
     if constexpr (NC > 0) {
 #pragma unroll
       for (int c = 0; c < NC; ++c)
-        if (c < iters) count(keys[c]);
+        if (c < iters) count1(keys[c]);
     } else {
       for (int c = 0; c < iters; ++c) {
         uint32_t kk[4];
         load_keys(c, kk);
-        count(kk);
+        count1(kk);
       }
     }
     __syncthreads();
-    if (pass == 0)
-      find_bin<C>(sh, nb, k_rem);
-    else
-      find_bin<1>(sh, nb, k_rem);
-    const uint32_t bin = sh.bin;
+    find_bin<C, true>(sh, sh.hist, kBins, k_rem);
     const uint32_t cnt = sh.cnt;
     k_rem -= sh.above;
-    prefix |= bin << sh_;
-    mask |= (uint32_t)(nb - 1) << sh_;
-    if (cnt == k_rem) {                           // the whole bin is taken
-      whole = true;
-      break;
+    prefix = sh.bin << 20;
+    mask = 0xfff00000u;
+    whole = cnt == k_rem;
+  }
+  if (!whole) {
+    for (int pass = 1; pass < 3; ++pass) {
+      const int sh_ = pass == 1 ? 8 : 0;
+      const int nb = pass == 1 ? kBins : 256;
+      uint32_t* const h = pass == 1 ? sh.hist : sh.h3;
+      // prefix == 0 only if pass 1 chose bin 0; only then can padding match
+      const bool check_pad = prefix == 0u;
+      auto count = [&](const uint32_t (&kk)[4]) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if ((kk[e] & mask) == prefix && (!check_pad || kk[e] != 0u))
+            atomicAdd(&h[(kk[e] >> sh_) & (nb - 1)], 1u);
+      };
+      if constexpr (NC > 0) {
+#pragma unroll
+        for (int c = 0; c < NC; ++c)
+          if (c < iters) count(keys[c]);
+      } else {
+        for (int c = 0; c < iters; ++c) {
+          uint32_t kk[4];
+          load_keys(c, kk);
+          count(kk);
+        }
+      }
+      __syncthreads();
+      find_bin<1, false>(sh, h, nb, k_rem);
+      const uint32_t cnt = sh.cnt;
+      k_rem -= sh.above;
+      prefix |= sh.bin << sh_;
+      mask |= (uint32_t)(nb - 1) << sh_;
+      if (cnt == k_rem) {                         // the whole bin is taken
+        whole = true;
+        break;
+      }
     }
   }
   // hist is free from here on (the last find_bin ended with a barrier and
@@ -391,10 +419,10 @@ __global__ __launch_bounds__(kThreads, NC == 2 ? 8 : 4) void topk_kernel(TopkLau
   if constexpr (NC > 0) {
     // Bitmaps: chunk c of thread t covers positions 4*(c*kThreads + t) + e,
     // so the 8 lanes t = 8m..8m+7 fill word c*kThreads/8 + m, 4 bits each.
-    // WHOLE: the last bin was taken whole, so the selection is simply
-    // key >= prefix (prefix != 0 excludes padding) and one bitmap suffices.
-    auto emit_bits = [&](auto whole_tag) {
-      constexpr bool WHOLE = decltype(whole_tag)::value;
+    // THR: one threshold, "above" = key > thr (no "equal" bitmap);
+    // otherwise "above" and "equal" by prefix and mask.
+    auto build_bits = [&](auto thr_tag, uint32_t thr) {
+      constexpr bool THR = decltype(thr_tag)::value;
       const int sub = lane & 7;
 #pragma unroll
       for (int c = 0; c < NC; ++c) {
@@ -402,8 +430,8 @@ __global__ __launch_bounds__(kThreads, NC == 2 ? 8 : 4) void topk_kernel(TopkLau
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const uint32_t k = keys[c][e];
-          if constexpr (WHOLE) {
-            gn |= k >= prefix ? (1u << e) : 0u;
+          if constexpr (THR) {
+            gn |= k > thr ? (1u << e) : 0u;
           } else {
             const uint32_t m = k & mask;
             const bool valid = k != 0u;
@@ -416,17 +444,23 @@ __global__ __launch_bounds__(kThreads, NC == 2 ? 8 : 4) void topk_kernel(TopkLau
         gw |= dpp<0x111, 0xf>(gw);
         gw |= dpp<0x112, 0xf>(gw);
         gw |= dpp<0x114, 0xf>(gw);
-        if (sub == 7) sh.gt_bits[c * (kThreads / 8) + (tid >> 3)] = gw;
-        if constexpr (!WHOLE) {
+        const int word = c * (kThreads / 8) + (tid >> 3);
+        if (sub == 7) sh.gt_bits[word] = gw;
+        if constexpr (!THR) {
           uint32_t ew = en << (4 * sub);
           ew |= dpp<0x111, 0xf>(ew);
           ew |= dpp<0x112, 0xf>(ew);
           ew |= dpp<0x114, 0xf>(ew);
-          if (sub == 7) sh.eq_bits[c * (kThreads / 8) + (tid >> 3)] = ew;
+          if (sub == 7) sh.eq_bits[word] = ew;
         }
       }
       __syncthreads();
-      // One thread per J consecutive words, in position order.
+    };
+    // One thread per J consecutive words, in position order: a block-wide
+    // scan of the word counts gives output slots; equal positions are taken
+    // while fewer than k_rem came before (EQ).
+    auto emit_words = [&](auto eq_tag) {
+      constexpr bool EQ = decltype(eq_tag)::value;
       constexpr int W = Shared<NC, C>::kWords;
       constexpr int J = W >= kThreads ? W / kThreads : 1;
       const bool act = tid * J < W;
@@ -434,26 +468,25 @@ __global__ __launch_bounds__(kThreads, NC == 2 ? 8 : 4) void topk_kernel(TopkLau
 #pragma unroll
       for (int j = 0; j < J; ++j) {
         gw[j] = act ? sh.gt_bits[tid * J + j] : 0u;
-        ew[j] = (!WHOLE && act) ? sh.eq_bits[tid * J + j] : 0u;
+        ew[j] = (EQ && act) ? sh.eq_bits[tid * J + j] : 0u;
         gc += __builtin_popcount(gw[j]);
-        if constexpr (!WHOLE) ec += __builtin_popcount(ew[j]);
+        if constexpr (EQ) ec += __builtin_popcount(ew[j]);
       }
       const uint32_t gi = wave_incl_scan(gc);
-      const uint32_t ei = WHOLE ? 0u : wave_incl_scan(ec);
+      const uint32_t ei = EQ ? wave_incl_scan(ec) : 0u;
       if (lane == 63) {
         sh.wsum[wave] = gi;
-        if constexpr (!WHOLE) sh.wsum[kWaves + wave] = ei;
+        if constexpr (EQ) sh.wsum[kWaves + wave] = ei;
       }
       __syncthreads();
       // counts before my first word
       uint32_t g_b = gi - gc + sum_before(sh.wsum, wave);
-      uint32_t e_b = WHOLE ? 0u : ei - ec + sum_before(sh.wsum + kWaves, wave);
+      uint32_t e_b = EQ ? ei - ec + sum_before(sh.wsum + kWaves, wave) : 0u;
 #pragma unroll
       for (int j = 0; j < J; ++j) {
         uint32_t sel = gw[j];
         uint32_t slot = g_b;
-        if constexpr (!WHOLE) {
-          // equal positions are taken while fewer than k_rem came before
+        if constexpr (EQ) {
           uint32_t ek = ew[j];
           if (e_b >= k_rem) {
             ek = 0u;
@@ -475,14 +508,18 @@ __global__ __launch_bounds__(kThreads, NC == 2 ? 8 : 4) void topk_kernel(TopkLau
           sel &= sel - 1u;
         }
         g_b += __builtin_popcount(gw[j]);
-        if constexpr (!WHOLE) e_b += __builtin_popcount(ew[j]);
+        if constexpr (EQ) e_b += __builtin_popcount(ew[j]);
       }
       __syncthreads();                            // the stage is complete
     };
-    if (whole && prefix != 0u)
-      emit_bits(std::true_type{});
-    else
-      emit_bits(std::false_type{});
+    if (whole && prefix != 0u) {
+      // the selection is key >= prefix (prefix != 0 excludes padding)
+      build_bits(std::true_type{}, prefix - 1u);
+      emit_words(std::false_type{});
+    } else {
+      build_bits(std::false_type{}, 0u);
+      emit_words(std::true_type{});
+    }
   } else {
     // Ordered emission: chunk c holds positions 4*(c*kThreads + tid) + 0..3,
     // so positions run over (chunk, thread, element).  A group of chunks is

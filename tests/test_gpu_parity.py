@@ -134,6 +134,11 @@ def _special_rows(kind, n_rows, n, seed):
         x = np.where(rng.random((n_rows, n)) < 0.5, 1.0, 2.0).astype(np.float32)
     elif kind == "subnormal":    # value range too small to scale into bins
         x = (rng.integers(-50, 50, (n_rows, n)) * 1.4e-45).astype(np.float32)
+    elif kind == "pivot_ties":   # a few hundred exact copies of a value near the K-th largest
+        x = (8.0 * rng.standard_normal((n_rows, n))).astype(np.float32)
+        for r in range(n_rows):
+            v = np.sort(x[r])[::-1][min(n - 1, int(0.07 * n))]
+            x[r, rng.choice(n, 300, replace=False)] = v
     elif kind == "huge_range":   # max - min overflows fp32
         x = rng.standard_normal((n_rows, n)).astype(np.float32)
         x[:, 0], x[:, 1] = 3.0e38, -3.0e38
@@ -142,7 +147,8 @@ def _special_rows(kind, n_rows, n, seed):
     return torch.from_numpy(x).to(DEV)
 
 
-@pytest.mark.parametrize("kind", ["inf", "outliers", "narrow", "equal", "two_values", "subnormal", "huge_range"])
+@pytest.mark.parametrize("kind", ["inf", "outliers", "narrow", "equal", "two_values", "subnormal", "huge_range",
+                                  "pivot_ties"])
 @pytest.mark.parametrize("Lk,K", [(6000, 2048), (30000, 2048), (50000, 100), (80000, 2048), (20000, 5000)])
 def test_topk_special_rows(kind, Lk, K):
     dsa = _dsa()
