@@ -176,17 +176,17 @@ __device__ __forceinline__ float reduce4(float p0, float p1, float p2, float p3)
 }
 
 // ------------------------------------------------------ decode shape -------
-// grid (ceil(Lk / 2048), B * q_count), 4 waves; wave w owns keys
-// [c0 + 512w, c0 + 512w + 512) of its query.  Keys stream through a private
-// 4-stage LDS ring of 16-key tiles filled by LDS-DMA (global_load_lds): each
-// copy instruction moves whole 256-byte (bf16) or 128-byte (fp8) key rows, so
-// every request is a full cache line, and no registers hold data in flight.
-// Within a staged row the 16-byte chunks are XOR-permuted by the row index,
-// which makes the MFMA operand reads conflict-free.  Scores collect in LDS
-// and leave with one coalesced store per wave, so the vector-memory counter
-// only tracks the copies.
+// grid (ceil(Lk / 2048), B * q_count), 4 waves; the work-group walks the
+// 16-key tiles of keys [c0, c0 + 2048) of its query in order, tile t going
+// to wave t % 4, so the four waves read one contiguous stream.  Each wave's
+// tiles pass through a private 4-stage LDS ring filled by LDS-DMA
+// (global_load_lds): each copy instruction moves whole 256-byte (bf16) or
+// 128-byte (fp8) key rows, so every request is a full cache line, and no
+// registers hold data in flight.  Within a staged row the 16-byte chunks are
+// XOR-permuted by the row index, which makes the MFMA operand reads
+// conflict-free.  Scores collect in LDS and leave with coalesced stores
+// after one barrier, so the vector-memory counter only tracks the copies.
 constexpr int kDecChunk = 2048;                  // keys per work-group
-constexpr int kDecPerWave = kDecChunk / 4;
 constexpr int kDecRing = 4;
 
 template <bool FP8>
@@ -197,25 +197,26 @@ __global__ __launch_bounds__(256, 2) void idx_decode_kernel(IndexLaunch a) {
   constexpr int STG = TK * ROWB;                 // bytes per stage
   constexpr int NDMA = STG / 1024;               // copy instructions per stage
   __shared__ __attribute__((aligned(16))) uint8_t ring[4][kDecRing][STG];
-  __shared__ __attribute__((aligned(16))) float sc[4][kDecPerWave];
-  __shared__ __attribute__((aligned(16))) uint8_t kscale[4][FP8 ? kDecPerWave : 16];
+  __shared__ __attribute__((aligned(16))) float sc[kDecChunk];
+  __shared__ __attribute__((aligned(16))) uint8_t kscale[FP8 ? kDecChunk : 16];
 
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int row = blockIdx.y;
   const int b = row / a.q_count;
   const int i = a.q_begin + row % a.q_count;
   const int n = a.Lk - a.Lq + i + 1;
-  const int w0 = blockIdx.x * kDecChunk + wave * kDecPerWave;
-  const int w1 = min(w0 + kDecPerWave, a.Lk);
-  const int wn = min(w1, n);
+  const int c0 = blockIdx.x * kDecChunk;
+  const int c1 = min(c0 + kDecChunk, a.Lk);
+  const int cn = min(c1, n);
   float* out = a.scores + (int64_t)row * a.row_stride;
   if (a.write_masked) {
-    for (int s = max(w0, n) + lane; s < w1; s += 64) out[s] = kNegInf;
+    for (int s = max(c0, n) + tid; s < c1; s += 256) out[s] = kNegInf;
     wait_vmcnt<0>();
   }
-  if (w0 >= wn) return;
-  const int nk = wn - w0;
-  const int nst = (nk + TK - 1) / TK;
+  if (c0 >= cn) return;                          // uniform over the work-group
+  const int nk = cn - c0;
+  const int ntile = (nk + TK - 1) / TK;
+  const int nst = (ntile - wave + 3) / 4;        // my tiles: wave, wave + 4, ...
 
   const int64_t qrow = (int64_t)b * a.Lq + i;
   const uint8_t* kbase = static_cast<const uint8_t*>(a.k) + (int64_t)b * a.Lc * ROWB;   // wave-uniform
@@ -231,7 +232,7 @@ __global__ __launch_bounds__(256, 2) void idx_decode_kernel(IndexLaunch a) {
   }
   const uint32_t ring_lds = lds_addr(&ring[wave][0][0]);
   auto issue = [&](int st) {
-    const int k0 = w0 + st * TK;
+    const int k0 = c0 + (4 * st + wave) * TK;
     const uint32_t dst = __builtin_amdgcn_readfirstlane(ring_lds + (st % kDecRing) * STG);
 #pragma unroll
     for (int k = 0; k < NDMA; ++k) {
@@ -245,7 +246,7 @@ __global__ __launch_bounds__(256, 2) void idx_decode_kernel(IndexLaunch a) {
     if (st < nst) issue(st);
   if constexpr (FP8) {
     const uint8_t* ks = a.k_scale + (int64_t)b * a.Lc;
-    for (int j = lane; j < nk; j += 64) kscale[wave][j] = ks[w0 + j];
+    for (int j = tid; j < nk; j += 256) kscale[j] = ks[c0 + j];
   }
   QFrag<FP8> q;
   float wv[16];
@@ -253,6 +254,7 @@ __global__ __launch_bounds__(256, 2) void idx_decode_kernel(IndexLaunch a) {
   // Wait for everything issued so far (the query loads are the youngest), so
   // that inside the loop only the copies use the vector-memory counter.
   wait_vmcnt<0>();
+  if constexpr (FP8) __syncthreads();            // the key scales are in LDS
   if constexpr (!FP8) {
 #pragma unroll
     for (int m = 0; m < 4; ++m)
@@ -283,15 +285,15 @@ __global__ __launch_bounds__(256, 2) void idx_decode_kernel(IndexLaunch a) {
       kf.v = join(ld16(lrow + (((2 * g) ^ (r16 & 7)) * 16)), ld16(lrow + (((2 * g + 1) ^ (r16 & 7)) * 16)));
     }
     float s = tile_score<FP8>(q, kf, wv);
-    const int j = st * TK + lane;
+    const int j = (4 * st + wave) * TK + lane;
     if (lane < TK) {
-      if constexpr (FP8) s *= ue8m0_to_f32(kscale[wave][min(j, kDecPerWave - 1)]);
-      sc[wave][j] = s;
+      if constexpr (FP8) s *= ue8m0_to_f32(kscale[min(j, kDecChunk - 1)]);
+      sc[j] = s;
     }
   }
-  // one coalesced store of this wave's scores
-  __builtin_amdgcn_s_waitcnt(0xc07f);            // lgkmcnt(0): own LDS writes done
-  for (int j = lane; j < nk; j += 64) out[w0 + j] = sc[wave][j];
+  // coalesced stores of the work-group's scores
+  __syncthreads();
+  for (int j = tid; j < nk; j += 256) out[c0 + j] = sc[j];
 }
 
 // ----------------------------------------------------- prefill shape -------
