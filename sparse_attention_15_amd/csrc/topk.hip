@@ -11,11 +11,13 @@
 // MSB-first radix select (12 + 12 + 8 bits, LDS histograms) finds the
 // threshold key T and how many elements equal to T are still needed (r).
 // Index scores crowd into a few exponents, so many lanes of one atomic
-// instruction hit the same bin; each histogram therefore keeps C copies
-// (lane l adds to copy l % C), laid out copy-major with a stride of 4096 + 4
-// words so the copies of one bin sit in different banks and a thread's run
-// of 4 bins is one aligned 16-byte read.
-// The selection is {key > T} plus the first r positions with key == T.
+// instruction hit the same bin; the first pass's histogram therefore keeps
+// C copies (lane l adds to copy l % C), laid out copy-major with a stride of
+// 4096 + 4 words so the copies of one bin sit in different banks and a
+// thread's run of 4 bins is one aligned 16-byte read.  Later passes count
+// one bin's elements into a single copy.
+// The selection is {key > T} plus the first r positions with key == T; when
+// the last pass takes its bin whole it is simply {key >= prefix}.
 // Rows held in registers (4 consecutive positions per 16-byte load) write
 // two bitmaps over positions, "above T" and "equal to T", one 32-position
 // word per 8 lanes (DPP OR of their 4-bit groups); one thread per word then
