@@ -89,7 +89,8 @@ ForwardPlan plan_forward(const dsa_problem_t& p, Path path, bool need_idx) {
   const int rows = p.batch * f.chunk;
   f.part_bytes = attn_partials_bytes(p, rows, attn_splits(p, path, rows));
   f.tk_slices = topk_slices(rows, p.kv_len, p.topk, &f.tk_slice_len);
-  f.cand_bytes = f.tk_slices > 1 ? align_up((size_t)rows * f.tk_slices * p.topk * 4) : 0;
+  // candidate positions and their scores
+  f.cand_bytes = f.tk_slices > 1 ? 2 * align_up((size_t)rows * f.tk_slices * p.topk * 4) : 0;
   return f;
 }
 
@@ -111,7 +112,7 @@ TopkLaunch make_topk(const dsa_problem_t& p, const float* scores, int64_t row_st
   a.B = p.batch; a.Lq = p.q_len; a.Lk = p.kv_len; a.K = p.topk;
   a.q_begin = q_begin; a.q_count = q_count;
   a.vec_ok = aligned16(scores) && (row_stride % 4) == 0;
-  a.slices = 1; a.slice_len = 0; a.cand = nullptr;
+  a.slices = 1; a.slice_len = 0; a.cand = nullptr; a.cand_score = nullptr;
   return a;
 }
 
@@ -204,6 +205,7 @@ dsa_status_t forward_impl(const dsa_problem_t* prob, const void* q_idx, const ui
       ta.slices = f.tk_slices;
       ta.slice_len = f.tk_slice_len;
       ta.cand = cand;
+      ta.cand_score = reinterpret_cast<float*>(reinterpret_cast<char*>(cand) + f.cand_bytes / 2);
     }
     if ((e = launch_topk(ta, stream)) != hipSuccess) return hip_status(e);
     if ((e = ev.rec(c, 1, 1)) != hipSuccess) return DSA_ERR_HIP;

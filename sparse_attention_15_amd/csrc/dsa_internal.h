@@ -32,8 +32,11 @@ struct TopkLaunch {
   int vec_ok;              // rows are 16-byte aligned: use 16-byte loads
   // two-stage selection (slices > 1): each row's slices of slice_len
   // positions first keep their own top K in cand [rows][slices][K]
+  // (positions, -1 for none) with their scores in cand_score (same shape),
+  // which the second stage reads in place of gathering them
   int slices, slice_len;
   int32_t* cand;
+  float* cand_score;
 };
 
 struct AttnLaunch {

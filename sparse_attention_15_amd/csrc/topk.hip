@@ -156,8 +156,8 @@ __device__ void find_bin(Shared<NC, C>& sh, const uint32_t* h, int nb, uint32_t 
 
 // Modes: kRows selects from score rows; kSlice (first of two stages for a
 // few long rows) selects the top K of each slice of a row into a candidate
-// list; kCand (second stage) selects from a row's candidate lists, reading
-// each candidate's score through its position.
+// list (positions, and the scores beside them); kCand (second stage)
+// selects from a row's candidate lists, reading their scores in order.
 enum { kRows = 0, kSlice = 1, kCand = 2 };
 
 // NC 16-byte chunks per thread kept in registers (0 = re-read each pass);
@@ -178,6 +178,7 @@ __global__ __launch_bounds__(kThreads, NC == 2 ? 8 : 4) void topk_kernel(TopkLau
   const int p0 = slice * a.slice_len;             // first position of the slice
   int n;                                          // elements to select from
   int32_t* out;
+  float* out_score = nullptr;                     // kSlice: the kept candidates' scores
   const int32_t* cand = nullptr;                  // kCand: this row's candidate positions
   if constexpr (MODE == kRows) {
     n = n_row;
@@ -186,9 +187,11 @@ __global__ __launch_bounds__(kThreads, NC == 2 ? 8 : 4) void topk_kernel(TopkLau
     n = max(0, min(a.slice_len, n_row - p0));
     src += p0;
     out = a.cand + ((int64_t)row * a.slices + slice) * K;
+    out_score = a.cand_score + ((int64_t)row * a.slices + slice) * K;
   } else {
     n = a.slices * K;
     cand = a.cand + (int64_t)row * a.slices * K;
+    src = a.cand_score + (int64_t)row * a.slices * K;   // element x's score
     out = a.out + ((int64_t)b * a.Lq + i) * K;
   }
   // position of element x of this selection in the row
@@ -203,7 +206,10 @@ __global__ __launch_bounds__(kThreads, NC == 2 ? 8 : 4) void topk_kernel(TopkLau
     return;
   }
   if (n <= K) {                                   // kCand never: n = slices * K > K
-    for (int j = tid; j < K; j += kThreads) out[j] = j < n ? pos_of(j) : -1;
+    for (int j = tid; j < K; j += kThreads) {
+      out[j] = j < n ? pos_of(j) : -1;
+      if constexpr (MODE == kSlice) out_score[j] = j < n ? src[j] : 0.f;
+    }
     return;
   }
   const int nchunks = (n + 3) >> 2;               // 4 positions per chunk
@@ -216,13 +222,14 @@ __global__ __launch_bounds__(kThreads, NC == 2 ? 8 : 4) void topk_kernel(TopkLau
       // candidates: a position, or -1 for an unused slot (key 0: never chosen)
       if (a.vec_ok && pos + 3 < n) {
         const u32x4 cv = ld16(cand + pos);
+        const f32x4 sv = *reinterpret_cast<const f32x4*>(src + pos);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) kk[e] = (int32_t)cv[e] >= 0 ? order_key(src[(int32_t)cv[e]]) : 0u;
+        for (int e = 0; e < 4; ++e) kk[e] = (int32_t)cv[e] >= 0 ? order_key(sv[e]) : 0u;
       } else {
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int32_t cx = pos + e < n ? cand[pos + e] : -1;
-          kk[e] = cx >= 0 ? order_key(src[cx]) : 0u;
+          kk[e] = cx >= 0 ? order_key(src[pos + e]) : 0u;
         }
       }
     } else {
@@ -252,34 +259,39 @@ __global__ __launch_bounds__(kThreads, NC == 2 ? 8 : 4) void topk_kernel(TopkLau
     const int crag = cfull < iters ? cfull : NC;  // the chunk loaded lane by lane
     auto inside = [&](int c, int e) { return c < cfull || (c < iters && (c * kThreads + tid) * 4 + e < n); };
     if (a.vec_ok && NC >= 8 && (MODE != kCand || NC <= 8)) {
+      // src: the row's scores, or (kCand) the candidates' scores in order
       float vr[4] = {0.f, 0.f, 0.f, 0.f};        // the ragged chunk
       int32_t ar[4] = {-1, -1, -1, -1};
       const int rpos = (crag * kThreads + tid) * 4;
       if (crag < NC) {                            // lanes wholly inside still take one load
-        if constexpr (MODE == kCand) {
-          if (rpos + 3 < n) {
+        if (rpos + 3 < n) {
+          const f32x4 t = *reinterpret_cast<const f32x4*>(src + rpos);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) vr[e] = t[e];
+          if constexpr (MODE == kCand) {
             const u32x4 cv = ld16(cand + rpos);
 #pragma unroll
             for (int e = 0; e < 4; ++e) ar[e] = (int32_t)cv[e];
-          } else {
-#pragma unroll
-            for (int e = 0; e < 4; ++e) ar[e] = rpos + e < n ? cand[rpos + e] : -1;
           }
         } else {
-          if (rpos + 3 < n) {
-            const f32x4 t = *reinterpret_cast<const f32x4*>(src + rpos);
-            vr[0] = t.x;
-            vr[1] = t.y;
-            vr[2] = t.z;
-            vr[3] = t.w;
-          } else {
 #pragma unroll
-            for (int e = 0; e < 4; ++e) vr[e] = rpos + e < n ? src[rpos + e] : 0.f;
+          for (int e = 0; e < 4; ++e) {
+            vr[e] = rpos + e < n ? src[rpos + e] : 0.f;
+            if constexpr (MODE == kCand) ar[e] = rpos + e < n ? cand[rpos + e] : -1;
           }
         }
       }
       float v[NC][4];
+#pragma unroll
+      for (int c = 0; c < NC; ++c) {
+        const f32x4 t = *reinterpret_cast<const f32x4*>(src + (c < cfull ? (c * kThreads + tid) * 4 : 0));
+        v[c][0] = t.x;
+        v[c][1] = t.y;
+        v[c][2] = t.z;
+        v[c][3] = t.w;
+      }
       if constexpr (MODE == kCand) {
+        // a candidate slot holds a position, or -1 for none (key 0)
         int32_t at[NC][4];
 #pragma unroll
         for (int c = 0; c < NC; ++c) {
@@ -287,24 +299,12 @@ __global__ __launch_bounds__(kThreads, NC == 2 ? 8 : 4) void topk_kernel(TopkLau
 #pragma unroll
           for (int e = 0; e < 4; ++e) at[c][e] = c < cfull ? (int32_t)cv[e] : (c == crag ? ar[e] : -1);
         }
-        // gathers (unused slots read position 0)
 #pragma unroll
         for (int c = 0; c < NC; ++c)
 #pragma unroll
-          for (int e = 0; e < 4; ++e) v[c][e] = src[max(at[c][e], 0)];
-#pragma unroll
-        for (int c = 0; c < NC; ++c)
-#pragma unroll
-          for (int e = 0; e < 4; ++e) keys[c][e] = at[c][e] >= 0 ? order_key(v[c][e]) : 0u;
+          for (int e = 0; e < 4; ++e)
+            keys[c][e] = at[c][e] >= 0 ? order_key(c < cfull ? v[c][e] : vr[e]) : 0u;
       } else {
-#pragma unroll
-        for (int c = 0; c < NC; ++c) {
-          const f32x4 t = *reinterpret_cast<const f32x4*>(src + (c < cfull ? (c * kThreads + tid) * 4 : 0));
-          v[c][0] = t.x;
-          v[c][1] = t.y;
-          v[c][2] = t.z;
-          v[c][3] = t.w;
-        }
 #pragma unroll
         for (int c = 0; c < NC; ++c)
 #pragma unroll
@@ -314,8 +314,8 @@ __global__ __launch_bounds__(kThreads, NC == 2 ? 8 : 4) void topk_kernel(TopkLau
     } else {
       // unaligned rows, short rows (one or two chunks: nothing to overlap,
       // and masked extra loads cost more than they hide), and the widest
-      // candidate lists (their gathers would not fit the registers at
-      // once): chunk by chunk
+      // candidate lists (positions and scores would not fit the registers
+      // at once): chunk by chunk
 #pragma unroll
       for (int c = 0; c < NC; ++c) {
         if (c < iters) load_keys(c, keys[c]);
@@ -413,8 +413,12 @@ __global__ __launch_bounds__(kThreads, NC == 2 ? 8 : 4) void topk_kernel(TopkLau
   const bool staged = K <= kBins;
   auto put = [&](uint32_t slot, int pos) {
     if (slot < (uint32_t)K) {                     // always, by construction
-      if (staged) sh.hist[slot] = (uint32_t)pos;
-      else out[slot] = pos;
+      if (staged) {
+        sh.hist[slot] = (uint32_t)pos;
+      } else {
+        out[slot] = pos;
+        if constexpr (MODE == kSlice) out_score[slot] = src[pos - p0];
+      }
     }
   };
 
@@ -592,6 +596,9 @@ __global__ __launch_bounds__(kThreads, NC == 2 ? 8 : 4) void topk_kernel(TopkLau
     } else {
       for (int j = tid; j < K; j += kThreads) out[j] = (int32_t)sh.hist[j];
     }
+    // the kept candidates' scores, re-read from the slice (just loaded)
+    if constexpr (MODE == kSlice)
+      for (int j = tid; j < K; j += kThreads) out_score[j] = src[(int)sh.hist[j] - p0];
   }
 }
 
