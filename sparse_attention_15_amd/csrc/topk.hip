@@ -627,15 +627,18 @@ void launch_mode(const TopkLaunch& a, int n_max, int grid, hipStream_t s) {
 int topk_slices(int rows, int n_max, int K, int* slice_len) {
   *slice_len = 0;
   // one work-group per row keeps one CU's VALU busy over the whole row; with
-  // fewer rows than CUs, split long rows: slices of about sqrt(n K)
-  // positions (stage 1 and stage 2 then each see a similar count).  Each
-  // stage has a fixed cost of a few microseconds (passes, barriers), so
-  // rows below 65536 positions stay single-stage (measured: 32768-position
-  // decode rows take 19.7 us in one stage, 24.6 us in two; 131072-position
-  // rows 82 us in one, 42 us in two).
+  // fewer rows than CUs, split long rows into slices of about sqrt(n K) / 2
+  // positions (more, shorter slices: the second stage reads its candidates'
+  // scores in order, so it costs little more per candidate than the first
+  // per position).  Each stage has a fixed cost of a few microseconds
+  // (passes, barriers), so rows below 65536 positions stay single-stage
+  // (measured: 32768-position decode rows take 19.7 us in one stage, 24.6
+  // us in two).  131072-position rows: 82 us in one stage; in two, 27.1 us
+  // with 8 slices of 16384, 25.3 us with 4 of 32768, 25.1 us with 16 of
+  // 8192.
   if (rows >= 256 || K > 4096 || (K & 3) || n_max < 4 * K || n_max < 65536) return 1;
   int len = 4096;
-  while ((int64_t)len * len < (int64_t)n_max * K) len *= 2;
+  while (4 * (int64_t)len * len < (int64_t)n_max * K) len *= 2;
   const int sl = (n_max + len - 1) / len;
   if (sl < 2 || (int64_t)sl * K > 65536) return 1;
   *slice_len = len;
