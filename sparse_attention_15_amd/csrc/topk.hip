@@ -632,8 +632,9 @@ int topk_slices(int rows, int n_max, int K, int* slice_len) {
   // scores in order, so it costs little more per candidate than the first
   // per position).  Each stage has a fixed cost of a few microseconds
   // (passes, barriers), so rows below 65536 positions stay single-stage
-  // (measured: 32768-position decode rows take 19.7 us in one stage, 24.6
-  // us in two).  131072-position rows: 82 us in one stage; in two, 27.1 us
+  // (measured: 32768-position decode rows take 15.6 us in one stage, 20.2
+  // us in two with 8 slices of 4096 and 23.9 with 4 of 8192).
+  // 131072-position rows: 82 us in one stage; in two, 27.1 us
   // with 8 slices of 16384, 25.3 us with 4 of 32768, 25.1 us with 16 of
   // 8192.
   if (rows >= 256 || K > 4096 || (K & 3) || n_max < 4 * K || n_max < 65536) return 1;
