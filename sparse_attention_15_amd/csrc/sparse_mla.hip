@@ -669,7 +669,12 @@ __global__ __launch_bounds__(256) void attn_f32_kernel(AttnLaunch a) {
 }  // namespace
 
 int attn_splits_bf16(int rows, int K) {
-  const int max_splits = (K + 63) / 64;           // at least 64 keys per split
+  // at least 128 keys (4 blocks) per split: a split's fixed costs (list, Q,
+  // first gathers, epilogue) and its 128 KB of partials for the combine
+  // outweigh the work of fewer keys (8 queries of 2048 keys: 32 splits of
+  // 64 keys 31.5 us attention + combine, 16 of 128 keys 29.3 us, 8 of 256
+  // keys 32.9 us)
+  const int max_splits = (K + 127) / 128;
   int s = 1;
   while (rows * s < 256 && s * 2 <= max_splits && s < 32) s *= 2;
   // a split's list window lives in LDS: at most kMaxPer entries (K <= 65536
