@@ -303,7 +303,7 @@ def test_forward_edge_shapes(case):
     dict(name="k5000_prefill", batch=1, q_len=6, kv_len=7000, topk=5000),
     # two-stage top-k (>= 65536 positions) with spare cache capacity
     dict(name="two_stage_capacity", batch=2, q_len=1, kv_len=70001, capacity=70100),
-    # FP8 index at 128K context: FP8 scores, two-stage top-k, 32 splits
+    # FP8 index at 128K context: FP8 scores, two-stage top-k, 16 splits
     dict(name="fp8_128k", batch=1, q_len=1, kv_len=131072, fp8=True),
 ])
 def test_forward_wide_cases(case):
