@@ -14,8 +14,10 @@
 // bf16).  The rotation runs as butterflies in fp32 in a fixed order: stages
 // h = 1, 2, 4 inside the lane, h = 8, 16, 32, 64 across lanes j ^ 1, 2, 4, 8,
 // then one multiply by fp32(1/sqrt(128)).  The scale exponent comes from the
-// bits of max|y| and the codes from integer rounding of the fp32 bits, so the
-// output is a pure function of the fp32 rotation.
+// bits of max|y|, and the codes from gfx950's fp32 -> E4M3 conversion
+// (v_cvt_pk_fp8_f32: OCP "fn" format, round to nearest even; a sweep of
+// every fp32 value of magnitude <= 448 matched that rule bit for bit), so
+// the output is a pure function of the fp32 rotation.
 #include "dsa_device.h"
 #include "dsa_internal.h"
 
@@ -23,32 +25,6 @@ namespace dsa {
 namespace {
 
 constexpr float kInvSqrt128 = 0x1.6a09e6p-4f;   // fp32(1/sqrt(128)) = 0x3db504f3
-
-// E4M3 ("fn") code of v, round to nearest / ties to even, |v| <= 448 assumed
-// (larger magnitudes saturate to 448).
-__device__ __forceinline__ uint32_t e4m3_rne(float v) {
-  const uint32_t u = __builtin_bit_cast(uint32_t, v);
-  const uint32_t sign = (u >> 24) & 0x80u;
-  const uint32_t au = u & 0x7fffffffu;
-  const float a = __builtin_bit_cast(float, au);
-  uint32_t code;
-  if (a < 0.015625f) {                            // below 2^-6: multiples of 2^-9
-    code = (uint32_t)__builtin_rintf(a * 512.0f); // 0..8; 8 is the code of 2^-6
-  } else {
-    int e = (int)(au >> 23) - 127;
-    const uint32_t m = au & 0x7fffffu;
-    uint32_t q = m >> 20;
-    const uint32_t rem = m & 0xfffffu;
-    if (rem > 0x80000u || (rem == 0x80000u && (q & 1u))) ++q;
-    if (q == 8u) {
-      q = 0u;
-      ++e;
-    }
-    const int ef = e + 7;
-    code = (ef > 15 || (ef == 15 && q == 7u)) ? 0x7eu : (((uint32_t)ef << 3) | q);
-  }
-  return sign | code;
-}
 
 // Smallest e with amax / 2^e <= 448 = 1.75 * 2^8, from the bits of amax:
 // amax = M * 2^E with M in [1, 2) gives e = E - 8 if M <= 1.75, else E - 7.
@@ -121,9 +97,14 @@ __global__ __launch_bounds__(256) void rotate_quant_kernel(const void* x, int64_
     for (int s = 1; s < 16; s <<= 1) amax = fmaxf(amax, __shfl_xor(amax, s, 64));
     const int e = scale_exp(amax);
     const float inv = __builtin_bit_cast(float, (uint32_t)(127 - e) << 23);   // 2^-e, exact
-    uint32_t c[2] = {0u, 0u};
+    // |v / 2^e| <= 448: every code is finite, no saturation involved
+    uint32_t c[2];
 #pragma unroll
-    for (int t = 0; t < 8; ++t) c[t >> 2] |= e4m3_rne(v[t] * inv) << (8 * (t & 3));
+    for (int q = 0; q < 2; ++q) {
+      int w = __builtin_amdgcn_cvt_pk_fp8_f32(v[4 * q] * inv, v[4 * q + 1] * inv, 0, false);
+      w = __builtin_amdgcn_cvt_pk_fp8_f32(v[4 * q + 2] * inv, v[4 * q + 3] * inv, w, true);
+      c[q] = (uint32_t)w;
+    }
     if (live) {
       *reinterpret_cast<u32x2*>(codes + row * 128 + 8 * j) = u32x2{c[0], c[1]};
       if (j == 0) scales[row] = (uint8_t)(e + 127);
