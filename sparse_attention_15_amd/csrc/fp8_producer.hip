@@ -77,13 +77,20 @@ __global__ __launch_bounds__(256) void rotate_quant_kernel(const void* x, int64_
           v[t] = a + b;
           v[t + h] = a - b;
         }
-    // stages h = 8, 16, 32, 64: element 8j + t pairs with lane j ^ (h / 8)
+    // stages h = 8, 16, 32, 64: element 8j + t pairs with lane j ^ (h / 8);
+    // lanes j ^ 1 and j ^ 2 are read by DPP quad permutations (no LDS trip)
 #pragma unroll
     for (int s = 1; s < 16; s <<= 1) {
       const bool upper = (j & s) != 0;
 #pragma unroll
       for (int t = 0; t < 8; ++t) {
-        const float o = __shfl_xor(v[t], s, 64);
+        float o;
+        if (s == 1)
+          o = __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v[t]), 0xB1, 0xf, 0xf, false));
+        else if (s == 2)
+          o = __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v[t]), 0x4E, 0xf, 0xf, false));
+        else
+          o = __shfl_xor(v[t], s, 64);
         v[t] = upper ? o - v[t] : v[t] + o;
       }
     }
