@@ -242,11 +242,18 @@ __global__ __launch_bounds__(256, 1) void gemm_big_kernel(GemmLaunch g) {
   __shared__ __attribute__((aligned(16))) uint8_t lds[NST * STAGE];
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave >> 1, wn = wave & 1;
-  const int n0 = blockIdx.x * BN, m0 = blockIdx.y * BM;
+  // Batch index fastest in launch order: consecutive work-groups take the
+  // same tile of consecutive batch entries, which for the per-head
+  // un-absorption are neighbouring 1 KB pieces of the same token rows (one
+  // stream instead of 128 strided ones).  Batch 1 keeps the grid order.
+  const int lin = blockIdx.x + gridDim.x * (blockIdx.y + gridDim.y * blockIdx.z);
+  const int bz = lin % g.batch, rest = lin / g.batch;
+  const int bx = rest % gridDim.x, by = rest / gridDim.x;
+  const int n0 = bx * BN, m0 = by * BM;
   const int nk = g.K / kGK;
   // uniform bases at this tile's first rows (per-lane offsets stay small)
-  const uint8_t* abase = reinterpret_cast<const uint8_t*>(g.A + (int64_t)blockIdx.z * g.sa + (int64_t)m0 * g.lda);
-  const uint8_t* bbase = reinterpret_cast<const uint8_t*>(g.B + (int64_t)blockIdx.z * g.sb + (int64_t)n0 * g.ldb);
+  const uint8_t* abase = reinterpret_cast<const uint8_t*>(g.A + (int64_t)bz * g.sa + (int64_t)m0 * g.lda);
+  const uint8_t* bbase = reinterpret_cast<const uint8_t*>(g.B + (int64_t)bz * g.sb + (int64_t)n0 * g.ldb);
   // copy c = wave * CPW + k (uniform) fills A rows if c < ACOPY, else B rows
   uint32_t off[CPW];
 #pragma unroll
@@ -309,7 +316,7 @@ __global__ __launch_bounds__(256, 1) void gemm_big_kernel(GemmLaunch g) {
   const int esz = g.c_f32 ? 4 : 2;
   const int pitch = TN * 4 + 16;                  // bytes per staged row (fp32 room, padded)
   uint8_t* ebuf = lds + wave * 32 * pitch;
-  uint8_t* cb = static_cast<uint8_t*>(g.C) + ((int64_t)blockIdx.z * g.sc) * esz;
+  uint8_t* cb = static_cast<uint8_t*>(g.C) + ((int64_t)bz * g.sc) * esz;
   const int row_bytes = TN * esz, chunks = 32 * row_bytes / 16;
 #pragma unroll
   for (int i = 0; i < IM; ++i) {
