@@ -123,6 +123,13 @@ __device__ __forceinline__ void lds_dma16(const void* gbase, uint32_t voff, uint
                  ::"s"(lds_base), "v"(voff), "s"(gbase)
                  : "m0");
 }
+// One byte per lane: lane l's byte at gbase + voff lands zero-extended in the
+// LDS dword at lds_base + 4*l (same ordering rules as lds_dma16).
+__device__ __forceinline__ void lds_dma_u8(const void* gbase, uint32_t voff, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_ubyte %1, %2"
+               ::"s"(lds_base), "v"(voff), "s"(gbase)
+               : "m0");
+}
 #pragma clang diagnostic pop
 
 // ue8m0 exponent byte -> 2^(e-127) as fp32 (e = 0 gives 2^-127, a subnormal).

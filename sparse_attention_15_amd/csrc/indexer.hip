@@ -141,16 +141,24 @@ __device__ __forceinline__ float tile_partial(const QFrag<FP8>& q, const KFrag<F
 #pragma unroll
       for (int m = 0; m < 4; ++m) acc[m] = mfma16(q.v[m][t], kf.v[t], acc[m]);
   } else {
+    // Scale operands 0 select the unscaled encoding (v_mfma_f32_16x16x128_f8f6f4),
+    // which issues faster than the scaled one; both give the plain E4M3
+    // products (bit-identical on gfx950).
 #pragma unroll
     for (int m = 0; m < 4; ++m)
-      acc[m] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(q.v[m], kf.v, acc[m], 0, 0, 0, 127, 0, 127);
+      acc[m] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(q.v[m], kf.v, acc[m], 0, 0, 0, 0, 0, 0);
   }
-  float s = 0.f;
+  // Two independent accumulation chains (head tiles 0-1 and 2-3), so that
+  // the dependent FMAs of one can issue between those of the other.
+  float s0 = 0.f, s1 = 0.f;
 #pragma unroll
-  for (int m = 0; m < 4; ++m)
+  for (int m = 0; m < 2; ++m)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) s = fmaf(wv[4 * m + j], relu<FP8>(acc[m][j]), s);
-  return s;
+    for (int j = 0; j < 4; ++j) {
+      s0 = fmaf(wv[4 * m + j], relu<FP8>(acc[m][j]), s0);
+      s1 = fmaf(wv[4 * m + 8 + j], relu<FP8>(acc[m + 2][j]), s1);
+    }
+  return s0 + s1;
 }
 
 // Scores of one 16-key tile for one query: returns the score of key r in
@@ -311,11 +319,12 @@ __global__ __launch_bounds__(256, 2) void idx_decode_kernel(IndexLaunch a) {
 // ----------------------------------------------------- prefill shape -------
 // grid (ceil(q_count / QB), ksplit, B), QB waves = QB consecutive queries.
 // The block walks 64-key tiles kt = blockIdx.y, +ksplit, ... up to the last
-// query's causal limit.  Tiles stream through a 4-deep LDS ring filled by
-// LDS-DMA (whole key rows per copy instruction, chunks XOR-permuted by row so
-// the MFMA operand reads are conflict-free); each tile is consumed by all QB
-// waves, with one barrier per tile.
-constexpr int kPreRing = 4;
+// query's causal limit.  Tiles stream through an LDS ring filled by LDS-DMA
+// (whole key rows per copy instruction, chunks XOR-permuted by row so the
+// MFMA operand reads are conflict-free); each tile is consumed by all QB
+// waves.  bf16: a 4-deep ring and one barrier per tile; FP8 tiles take half
+// the time, so they go two per barrier through a 6-deep ring.  Either way two
+// tiles are in flight while the current ones are consumed.
 
 template <bool FP8, int QB>
 __global__ __launch_bounds__(QB * 64) void idx_prefill_kernel(IndexLaunch a, int ksplit) {
@@ -326,7 +335,13 @@ __global__ __launch_bounds__(QB * 64) void idx_prefill_kernel(IndexLaunch a, int
   constexpr int NDMA = STG / 1024;                // copy instructions per tile
   static_assert(NDMA % QB == 0 || QB % NDMA == 0, "tile copies must split evenly over the waves");
   constexpr int DPW = NDMA >= QB ? NDMA / QB : 1; // copies per wave (waves >= NDMA issue none)
-  __shared__ __attribute__((aligned(16))) uint8_t ring[kPreRing][STG];
+  constexpr int STEP = FP8 ? 2 : 1;               // tiles per barrier
+  constexpr int RING = 2 * STEP + 2;              // ring slots
+  __shared__ __attribute__((aligned(16))) uint8_t ring[RING][STG];
+  // FP8: the tile's 64 key-scale bytes, one dword per key, copied by wave
+  // QB - 1 next to its share of the tile (no register load whose wait would
+  // also wait for the tiles in flight)
+  __shared__ __attribute__((aligned(16))) uint32_t kscl[FP8 ? RING : 1][TK];
 
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int qb = gridDim.x - 1 - blockIdx.x;      // longest rows first
@@ -355,19 +370,25 @@ __global__ __launch_bounds__(QB * 64) void idx_prefill_kernel(IndexLaunch a, int
     dchk[k] = (slot % CPR) ^ (drow[k] & (CPR - 1));
   }
   const bool copies = wave * DPW < NDMA;
+  static_assert(!FP8 || (QB - 1) * DPW < NDMA, "the scale-copying wave also copies key rows");
+  const bool scl = FP8 && wave == QB - 1;         // copies DPW + 1 per tile
   const uint32_t ring_lds = lds_addr(&ring[0][0]);
+  const uint32_t kscl_lds = lds_addr(&kscl[0][0]);
   auto issue = [&](int j) {
     if (!copies) return;
     const int k0 = (blockIdx.y + ksplit * j) * TK;
-    const uint32_t dst = __builtin_amdgcn_readfirstlane(ring_lds + (j % kPreRing) * STG);
+    const uint32_t dst = __builtin_amdgcn_readfirstlane(ring_lds + (j % RING) * STG);
 #pragma unroll
     for (int k = 0; k < DPW; ++k) {
       const int key = min(k0 + drow[k], a.Lk - 1);   // rows past the end repeat the last key
       lds_dma16(kbase, (uint32_t)key * ROWB + dchk[k] * 16, dst + 1024 * (wave * DPW + k));
     }
+    if (scl)
+      lds_dma_u8(ks, (uint32_t)min(k0 + lane, a.Lk - 1),
+                 __builtin_amdgcn_readfirstlane(kscl_lds + (j % RING) * (TK * 4)));
   };
 #pragma unroll
-  for (int j = 0; j < kPreRing - 1; ++j)
+  for (int j = 0; j < RING - STEP; ++j)
     if (j < nj) issue(j);
 
   QFrag<FP8> q;
@@ -377,44 +398,58 @@ __global__ __launch_bounds__(QB * 64) void idx_prefill_kernel(IndexLaunch a, int
                                                   // score stores use the counter from here on
 
   const int r16 = lane & 15, g = lane >> 4;
-  for (int j = 0; j < nj; ++j) {
-    // tile j is complete once at most this wave's copies of the later tiles
-    // remain (score stores, which may also be outstanding, only make the
-    // wait stricter)
-    if (copies) {
-      if (j + 2 < nj) wait_vmcnt<2 * DPW>();
-      else if (j + 1 < nj) wait_vmcnt<DPW>();
+  // wait until at most `later` tiles of this wave's copies are in flight
+  // (score stores, which may also be outstanding, only make the wait stricter)
+  auto wait_tiles = [&](int later) {
+    if (scl) {
+      if (later >= 2) wait_vmcnt<2 * (DPW + 1)>();
+      else if (later == 1) wait_vmcnt<DPW + 1>();
+      else wait_vmcnt<0>();
+    } else if (copies) {
+      if (later >= 2) wait_vmcnt<2 * DPW>();
+      else if (later == 1) wait_vmcnt<DPW>();
       else wait_vmcnt<0>();
     }
-    __builtin_amdgcn_s_barrier();                 // every wave's copies of tile j landed, tile j-1 is free
-    asm volatile("" ::: "memory");
-    if (j + kPreRing - 1 < nj) issue(j + kPreRing - 1);
+  };
+  auto tile_scores = [&](int j) {                 // this wave's scores of tile j
     const int kt = blockIdx.y + ksplit * j;
-    if (active && kt * TK <= p) {
-      const uint8_t* tile = &ring[j % kPreRing][0];
-      float part[TK / 16];                         // this lane's parts of the 4 sub-tiles
+    if (!active || kt * TK > p) return;
+    const uint8_t* tile = &ring[j % RING][0];
+    float part[TK / 16];                           // this lane's parts of the 4 sub-tiles
 #pragma unroll
-      for (int st = 0; st < TK / 16; ++st) {
-        const int rr = 16 * st + r16;
-        const uint8_t* lrow = tile + rr * ROWB;
-        KFrag<FP8> kf;
-        if constexpr (!FP8) {
+    for (int st = 0; st < TK / 16; ++st) {
+      const int rr = 16 * st + r16;
+      const uint8_t* lrow = tile + rr * ROWB;
+      KFrag<FP8> kf;
+      if constexpr (!FP8) {
 #pragma unroll
-          for (int t = 0; t < 4; ++t) kf.v[t] = ld16(lrow + (((4 * t + g) ^ (rr & 15)) * 16));
-        } else {
-          kf.v = join(ld16(lrow + (((2 * g) ^ (rr & 7)) * 16)), ld16(lrow + (((2 * g + 1) ^ (rr & 7)) * 16)));
-        }
-        part[st] = tile_partial<FP8>(q, kf, wv);
+        for (int t = 0; t < 4; ++t) kf.v[t] = ld16(lrow + (((4 * t + g) ^ (rr & 15)) * 16));
+      } else {
+        kf.v = join(ld16(lrow + (((2 * g) ^ (rr & 7)) * 16)), ld16(lrow + (((2 * g + 1) ^ (rr & 7)) * 16)));
       }
-      // lane 16 g + r16 gets the score of key 16 g + r16
-      float mine = reduce4(part[0], part[1], part[2], part[3]);
-      // one 256-byte store per tile and wave
-      const int key = kt * TK + lane;
-      if (key <= p) {
-        if constexpr (FP8) mine *= ue8m0_to_f32(ks[key]);
-        out[key] = mine;
-      }
+      part[st] = tile_partial<FP8>(q, kf, wv);
     }
+    // lane 16 g + r16 gets the score of key 16 g + r16
+    float mine = reduce4(part[0], part[1], part[2], part[3]);
+    // one 256-byte store per tile and wave
+    const int key = kt * TK + lane;
+    if (key <= p) {
+      if constexpr (FP8) mine *= ue8m0_to_f32(kscl[j % RING][lane]);
+      out[key] = mine;
+    }
+  };
+  for (int j0 = 0; j0 < nj; j0 += STEP) {
+    // tiles j0 .. j0 + STEP - 1 complete; tiles up to j0 + RING - STEP - 1
+    // were issued
+    wait_tiles(max(0, min(nj, j0 + RING - STEP) - (j0 + STEP)));
+    __builtin_amdgcn_s_barrier();                 // every wave's copies landed; the previous tiles are free
+    asm volatile("" ::: "memory");
+#pragma unroll
+    for (int u = 0; u < STEP; ++u)
+      if (j0 + RING - STEP + u < nj) issue(j0 + RING - STEP + u);
+    tile_scores(j0);
+    if constexpr (STEP == 2)
+      if (j0 + 1 < nj) tile_scores(j0 + 1);
   }
   if (a.write_masked && active && blockIdx.y == 0)
     for (int s = p + 1 + lane; s < a.Lk; s += 64) out[s] = kNegInf;
