@@ -85,6 +85,37 @@ def test_index_scores(name):
     assert err.max() <= tol_for(cfg)
 
 
+@pytest.mark.parametrize("base,case", [
+    # prefill-shaped launches (more than 4 queries) on ragged tile counts:
+    # a single partial 64-key tile, tiles fewer than the ring holds, odd and
+    # even tile counts per work-group, several sequences
+    ("fp8", dict(batch=1, q_len=5, kv_len=5)),
+    ("fp8", dict(batch=2, q_len=9, kv_len=70)),
+    ("fp8", dict(batch=1, q_len=33, kv_len=129)),
+    ("fp8", dict(batch=3, q_len=17, kv_len=1000)),
+    ("fp8", dict(batch=1, q_len=300, kv_len=4500)),
+    ("bf16", dict(batch=2, q_len=9, kv_len=70)),
+    ("bf16", dict(batch=1, q_len=33, kv_len=129)),
+    ("bf16", dict(batch=3, q_len=17, kv_len=1000)),
+])
+def test_index_scores_ragged_prefill(base, case):
+    dsa = _dsa()
+    cfg = C.scaled(C.PREFILL_64K_FP8 if base == "fp8" else C.PREFILL_8K, name=f"ragged_{base}", plant_count=0,
+                   **case)
+    inp, host = _inputs(cfg)
+    p = dsa.make_problem(cfg)
+    sc = dsa.index_scores(p, inp["q_idx"], inp["q_scale"], inp["k_idx"], inp["k_scale"], inp["head_w"])
+    torch.cuda.synchronize()
+    got = sc.cpu().numpy().astype(np.float64)
+    qf, kf = O.as_f64_index_inputs(host["q_idx"], host["q_scale"], host["k_idx"], host["k_scale"])
+    ref = O.index_scores(qf, kf, host["head_w"], cfg.q_len, cfg.kv_len)
+    fin = np.isfinite(ref)
+    assert np.array_equal(np.isneginf(got), ~fin), "causal -inf pattern differs"
+    err = np.abs(got[fin] - ref[fin])
+    print(f"{base} {case}: max |score err| {err.max():.3g}, max |score| {np.abs(ref[fin]).max():.3g}")
+    assert err.max() <= tol_for(cfg)
+
+
 @pytest.mark.parametrize("shape", [
     # (B, Lq, Lk, K, stride_pad, ties, negzero)
     (2, 5, 3000, 64, 0, 0.0, False),
