@@ -64,6 +64,28 @@ def test_workspace_size_is_host_only_and_sane(dsa):
     assert dsa.forward_chunks(dsa.make_problem(C.PREFILL_8K)) == 1
 
 
+def test_attention_split_plan_is_host_only_and_bounded(dsa):
+    # decode shapes split each query's list over work-groups until the launch
+    # fills the GPU's 256 CUs, with at least 128 keys per split; prefill
+    # shapes already have one work-group per query and never split
+    assert dsa.attn_splits(dsa.make_problem(C.DECODE_32K)) == 8      # 32 rows x 8 = 256
+    assert dsa.attn_splits(dsa.make_problem(C.DECODE_128K)) == 16    # 8 rows x 16 = 128, capped by K / 128
+    assert dsa.attn_splits(dsa.make_problem(C.PREFILL_8K)) == 1
+    assert dsa.attn_splits(dsa.make_problem(C.PREFILL_64K_FP8)) == 1
+    for batch in (1, 2, 3, 5, 8, 31, 64, 300):
+        for topk in (1, 16, 100, 2048, 5000, 65536):
+            p = _prob(dsa, C.DECODE_32K, batch=batch, topk=topk, kv_len=max(topk, 4096))
+            s = dsa.attn_splits(p)
+            assert s >= 1 and s & (s - 1) == 0 and s <= 32, (batch, topk, s)
+            per = -(-topk // s)
+            assert -(-per // 32) * 32 <= 2048, (batch, topk, s)       # one split's window fits in LDS
+            if topk <= 4096:
+                assert per >= min(128, topk), (batch, topk, s)               # at least 128 keys per split
+            if batch * s > 256 and topk <= 65536 // 32:
+                assert s == 1 or batch * s // 2 < 256, (batch, topk, s)     # no doubling past a full GPU
+    assert dsa.attn_splits(_prob(dsa, C.DECODE_32K, q_len=0)) == 0
+
+
 def _call_forward(dsa, p, ptr=16, ws_bytes=1 << 40, q_scale=None):
     L = dsa.lib()
     v = ctypes.c_void_p(ptr)
