@@ -304,11 +304,11 @@ __global__ __launch_bounds__(kWavesA * 64, 1) void attn_bf16_kernel(AttnLaunch a
   const int nent = max(0, min(a.K, j0 + per) - j0);
 
   // This split's list entries (all loads in flight at once), then the Q rows
-  // of this wave's 32 heads as one 32-row gather into a stage buffer (whole
-  // cache lines; read back with the key rows' conflict-free addressing).
-  // Four buffers: every wave now, into its own buffer.  Three: waves 0-2 now
-  // into buffers 0-2, wave 3 after the first barrier into buffer 2, while
-  // blocks 0 and 1 are gathered into buffers 0 and 1.
+  // of this wave's 32 heads staged in a stage buffer (read back with the key
+  // rows' conflict-free addressing).  Four buffers: every wave now, into its
+  // own buffer.  Three: waves 0-2 now into buffers 0-2 by LDS-DMA (whole
+  // cache lines), wave 3 after the first barrier into buffer 2, while blocks
+  // 0 and 1 are gathered into buffers 0 and 1.
   constexpr int kFillIt = MAXPER / (kWavesA * 64);
   int pv[kFillIt];
   const int32_t* idx = a.idx + qrow * a.K + j0;
@@ -331,7 +331,17 @@ __global__ __launch_bounds__(kWavesA * 64, 1) void attn_bf16_kernel(AttnLaunch a
       lds_dma16<false>(qwave, off, dst + k * 1024);
     }
   };
-  if (NST == 4 || wave < 3) gather_q(wave);
+  // Four buffers (decode splits): every wave loads its 36 KB of Q rows into
+  // registers with coalesced 16-byte loads, all in flight at once, and
+  // writes them to its buffer below (LDS-DMA copies would queue behind the
+  // few a wave keeps in flight).
+  if (NST == 4) {
+    const u32x4* qsrc = reinterpret_cast<const u32x4*>(qwave);
+#pragma unroll
+    for (int k = 0; k < kQSteps; ++k) st.qf[k] = qsrc[k * 64 + lane];
+  } else if (wave < 3) {
+    gather_q(wave);
+  }
   // Chosen rows into LDS as byte offsets (row * 1152; skipped and padding
   // entries point at row 0), one validity bit per entry in bmask (bit j of
   // word w: entry 32w + j is usable), and each wave's last usable entry.
@@ -375,7 +385,18 @@ __global__ __launch_bounds__(kWavesA * 64, 1) void attn_bf16_kernel(AttnLaunch a
 #pragma unroll
     for (int t = 0; t < kQSteps; ++t) st.qf[t] = ld16(qbuf + qk_off[t & 1] + 64 * (t >> 1));
   };
-  if (NST == 4 || wave < 3) {
+  if (NST == 4) {
+    // register k of lane l holds 16-byte chunk 64k + l of the wave's rows:
+    // row f / 72, chunk f % 72, stored at the chunk's permuted slot
+    uint8_t* qbuf = stg + wave * kStageBytes;
+#pragma unroll
+    for (int k = 0; k < kQSteps; ++k) {
+      const int f = k * 64 + lane;
+      const int r = f / kChunks, c = f - r * kChunks;
+      *reinterpret_cast<u32x4*>(qbuf + r * kLdsRow + 16 * (c ^ swz(r))) = st.qf[k];
+    }
+    read_q(wave);
+  } else if (wave < 3) {
     wait_vmcnt<0>();                              // this wave's Q rows have landed
     read_q(wave);
   }
