@@ -13,8 +13,8 @@
 // the ReLU-weighted head reduction happens in registers: 16 values per lane,
 // then two cross-lane adds.  Keys are read once per query group: through a
 // per-wave LDS-DMA ring of whole key rows for decode-shaped launches, through
-// a 4-deep LDS-DMA ring of swizzled 64-key tiles shared by 8 queries for
-// prefill-shaped ones.
+// an LDS-DMA ring of swizzled 64-key tiles shared by 8 queries for
+// prefill-shaped ones (4 slots for bf16, 6 for FP8).
 // FP8 (E4M3 codes + ue8m0 row scales): the MFMA consumes raw codes; the
 // query-row scales fold into the head weights and the key scale multiplies
 // the head sum.  Both are powers of two and ReLU is positively homogeneous,
