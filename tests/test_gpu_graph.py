@@ -6,7 +6,8 @@ replay it per step with fresh inputs copied into the captured buffers.  The
 library makes no allocation, memset or synchronisation inside the forward, so
 the captured launches are the eager ones; these tests check that every replay,
 with eager work and synchronisations between replays, gives exactly the eager
-result for the inputs then in the buffers.
+result for the inputs then in the buffers, for decode shapes (split lists
+and the combine launch) and prefill shapes.
 """
 import pytest
 import torch
@@ -26,6 +27,9 @@ CASES = {
     # FP8 index path, several splits.
     "decode128k_b2_L9000": C.scaled(C.DECODE_128K, name="decode128k_b2_L9000", batch=2, kv_len=9000,
                                     plant_count=16),
+    # prefill-shaped launches: rows shorter and longer than K, no split
+    "prefill_q77_L3000": C.scaled(C.PREFILL_8K, name="prefill_q77_L3000", q_len=77, kv_len=3000),
+    "fp8_prefill_q40_L3000": C.scaled(C.PREFILL_64K_FP8, name="fp8_prefill_q40_L3000", q_len=40, kv_len=3000),
 }
 
 
