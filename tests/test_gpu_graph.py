@@ -98,3 +98,36 @@ def test_forward_graph_replay_matches_eager(name):
         assert _same(g_lse, e_lse), f"{name} set {set_index}: lse differs from eager"
         assert bool(torch.isfinite(g_out.float()).all())
         assert int(g_idx.min()) >= -1
+
+
+def test_forwards_on_two_streams_equal_sequential_calls():
+    # the library keeps no mutable global state: two calls in flight on two
+    # streams (default priority) give what each gives alone
+    import sparse_attention_15_amd as dsa
+    cfg_a = CASES["decode_b3_L5000"]
+    cfg_b = CASES["prefill_q77_L3000"]
+    res = {}
+    for cfg in (cfg_a, cfg_b):
+        inp = generate(cfg, device=DEV, set_index=5)
+        p = dsa.make_problem(cfg)
+        lse = torch.empty(cfg.batch, cfg.q_len, cfg.attn_heads, dtype=torch.float32, device=DEV)
+        idx = torch.empty(cfg.batch, cfg.q_len, cfg.topk, dtype=torch.int32, device=DEV)
+        ws = torch.empty(max(dsa.workspace_size(p, dsa.DSA_OP_FORWARD), 1), dtype=torch.uint8, device=DEV)
+        out, lse, idx = dsa.forward(p, *(inp[k] for k in NAMES), lse=lse, topk_idx=idx, workspace=ws)
+        torch.cuda.synchronize()
+        res[cfg.name] = (inp, p, ws, out.clone(), lse.clone(), idx.clone())
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    got = {}
+    torch.cuda.synchronize()
+    for _ in range(3):
+        for st, cfg in zip(streams, (cfg_a, cfg_b)):
+            inp, p, ws, *_ = res[cfg.name]
+            with torch.cuda.stream(st):
+                lse = torch.empty(cfg.batch, cfg.q_len, cfg.attn_heads, dtype=torch.float32, device=DEV)
+                idx = torch.empty(cfg.batch, cfg.q_len, cfg.topk, dtype=torch.int32, device=DEV)
+                got[cfg.name] = dsa.forward(p, *(inp[k] for k in NAMES), lse=lse, topk_idx=idx, workspace=ws)
+        torch.cuda.synchronize()
+        for cfg in (cfg_a, cfg_b):
+            _, _, _, out, lse, idx = res[cfg.name]
+            g_out, g_lse, g_idx = got[cfg.name]
+            assert _same(g_idx, idx) and _same(g_out, out) and _same(g_lse, lse), cfg.name
