@@ -376,8 +376,13 @@ hipError_t launch_gemm_bt(const GemmLaunch& g, hipStream_t s) {
       hipLaunchKernelGGL(gemm_skinny_kernel<16>, grid, dim3(1024), 0, s, g);
   } else if (g.M >= 256 && g.N >= 128 && g.K % kGK == 0 && g.N % 8 == 0 && g.ldc % 8 == 0 &&
              (g.sc * (g.c_f32 ? 4 : 2)) % 16 == 0 && (reinterpret_cast<uintptr_t>(g.C) & 15) == 0) {
-    dim3 grid((g.N + 127) / 128, (g.M + 255) / 256, g.batch);
-    hipLaunchKernelGGL((gemm_big_kernel<128, 3>), grid, dim3(256), 0, s, g);
+    if (g.batch == 1 && g.N >= 1024) {
+      dim3 grid((g.N + 255) / 256, (g.M + 255) / 256, g.batch);
+      hipLaunchKernelGGL((gemm_big_kernel<256, 2>), grid, dim3(256), 0, s, g);
+    } else {
+      dim3 grid((g.N + 127) / 128, (g.M + 255) / 256, g.batch);
+      hipLaunchKernelGGL((gemm_big_kernel<128, 3>), grid, dim3(256), 0, s, g);
+    }
   } else if (g.M >= 128 && g.N >= 128) {
     dim3 grid((g.N + 127) / 128, (g.M + 127) / 128, g.batch);
     hipLaunchKernelGGL((gemm_tile_kernel<64, 64>), grid, dim3(256), 0, s, g);
