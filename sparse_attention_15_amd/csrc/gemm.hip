@@ -231,17 +231,17 @@ __global__ __launch_bounds__(256) void gemm_split_reduce_kernel(GemmLaunch g) {
 // point; 256 x BN halves it.  64-k stages move global -> LDS by LDS-DMA (no
 // registers), with the chunk permutation applied on the source side; NST stages in a ring, NST - 1 in flight, one barrier per stage.  The
 // output leaves through LDS, 16 bytes per lane along rows.
-template <int BN, int NST>
-__global__ __launch_bounds__(256, 1) void gemm_big_kernel(GemmLaunch g) {
-  constexpr int BM = 256, TM = 128, TN = BN / 2, IM = TM / 32, IN = TN / 32;
+template <int BN, int NST, int W>
+__global__ __launch_bounds__(W * 64, W / 4) void gemm_big_kernel(GemmLaunch g) {
+  constexpr int BM = 256, TM = 128, TN = BN / (W / 2), IM = TM / 32, IN = TN / 32;
   constexpr int STAGE = (BM + BN) * 128;          // bytes per stage: rows of 64 bf16
   constexpr int NCOPY = STAGE / 1024;             // 1 KB copies per stage
-  constexpr int CPW = NCOPY / 4;                  // per wave
+  constexpr int CPW = NCOPY / W;                  // per wave
   constexpr int ACOPY = BM * 128 / 1024;          // the first ACOPY copies fill A rows
-  static_assert(NCOPY % 4 == 0, "copies split evenly over the waves");
+  static_assert(NCOPY % W == 0, "copies split evenly over the waves");
   __shared__ __attribute__((aligned(16))) uint8_t lds[NST * STAGE];
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave / (W / 2), wn = wave % (W / 2);
   // Batch index fastest in launch order: consecutive work-groups take the
   // same tile of consecutive batch entries, which for the per-head
   // un-absorption are neighbouring 1 KB pieces of the same token rows (one
@@ -378,10 +378,10 @@ hipError_t launch_gemm_bt(const GemmLaunch& g, hipStream_t s) {
              (g.sc * (g.c_f32 ? 4 : 2)) % 16 == 0 && (reinterpret_cast<uintptr_t>(g.C) & 15) == 0) {
     if (g.batch == 1 && g.N >= 1024) {
       dim3 grid((g.N + 255) / 256, (g.M + 255) / 256, g.batch);
-      hipLaunchKernelGGL((gemm_big_kernel<256, 2>), grid, dim3(256), 0, s, g);
+      hipLaunchKernelGGL((gemm_big_kernel<256, 2, 8>), grid, dim3(512), 0, s, g);
     } else {
       dim3 grid((g.N + 127) / 128, (g.M + 255) / 256, g.batch);
-      hipLaunchKernelGGL((gemm_big_kernel<128, 3>), grid, dim3(256), 0, s, g);
+      hipLaunchKernelGGL((gemm_big_kernel<128, 3, 4>), grid, dim3(256), 0, s, g);
     }
   } else if (g.M >= 128 && g.N >= 128) {
     dim3 grid((g.N + 127) / 128, (g.M + 127) / 128, g.batch);
