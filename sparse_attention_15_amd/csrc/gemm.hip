@@ -381,7 +381,7 @@ hipError_t launch_gemm_bt(const GemmLaunch& g, hipStream_t s) {
       hipLaunchKernelGGL((gemm_big_kernel<256, 2, 8>), grid, dim3(512), 0, s, g);
     } else {
       dim3 grid((g.N + 127) / 128, (g.M + 255) / 256, g.batch);
-      hipLaunchKernelGGL((gemm_big_kernel<128, 3, 4>), grid, dim3(256), 0, s, g);
+      hipLaunchKernelGGL((gemm_big_kernel<128, 3, 8>), grid, dim3(512), 0, s, g);
     }
   } else if (g.M >= 128 && g.N >= 128) {
     dim3 grid((g.N + 127) / 128, (g.M + 127) / 128, g.batch);
