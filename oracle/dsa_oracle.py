@@ -232,11 +232,14 @@ def forward(q_idx, q_scale, k_idx, k_scale, head_w, q_attn, kv, topk_k: int, sca
 
 
 def forward_rows(q_idx, q_scale, k_idx, k_scale, head_w, q_attn, kv, rows, q_len: int,
-                 topk_k: int, scale: float, v_dim: int):
+                 topk_k: int, scale: float, v_dim: int, kv_len: int | None = None):
     """The whole path for a chosen list of (b, i) query rows only.
 
-    q_idx/head_w/q_attn are indexed [b, i]; k_idx/kv are the full caches
-    [B, Lk, ...].  Returns a list of dicts (scores [n], topk [K], out, lse).
+    q_idx/head_w/q_attn are indexed [b, i]; k_idx/kv are the caches
+    [B, >= Lk, ...].  kv_len is the context Lk (default: the caches' length);
+    cache slots at or beyond it are never read.  Returns a list of dicts
+    (scores [n], topk [K], out, lse), the same values forward() gives for
+    those rows.
     """
     res = []
     for (b, i) in rows:
@@ -246,8 +249,8 @@ def forward_rows(q_idx, q_scale, k_idx, k_scale, head_w, q_attn, kv, rows, q_len
         else:
             qi = np.asarray(q_idx[b, i], dtype=np.float64)
             kb = np.asarray(k_idx[b], dtype=np.float64)
-        kv_len = kb.shape[0]
-        n = visible_count(q_len, kv_len, i)
+        Lk = kb.shape[0] if kv_len is None else kv_len
+        n = visible_count(q_len, Lk, i)
         sc = index_scores_row(qi, kb, np.asarray(head_w[b, i], dtype=np.float64), n)
         sel = topk_row(sc, n, topk_k)
         o, l = sparse_attention_row(np.asarray(q_attn[b, i], dtype=np.float64),

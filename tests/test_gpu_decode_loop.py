@@ -129,9 +129,13 @@ def test_decode_loop_matches_causal_rows(name):
         for b in range(cfg.batch):
             r = ref[(b, t)]
             n = L0 + t + 1
-            ok, swaps, msg = O.topk_band_check(r["scores"], idx[b, 0].cpu().numpy(), n, cfg.topk)
+            sel = idx[b, 0].cpu().numpy()
+            ok, swaps, msg = O.topk_band_check(r["scores"], sel, n, cfg.topk)
             assert ok, f"step {t} seq {b}: {msg}"
-            if swaps and tol < 1e-3:
-                continue
-            assert np.abs(np64(out[b, 0]) - r["out"]).max() <= tol, f"step {t} seq {b}"
-            assert np.abs(lse[b, 0].cpu().numpy() - r["lse"]).max() <= tol, f"step {t} seq {b}"
+            ref_o, ref_l = r["out"], r["lse"]
+            if swaps:
+                # the oracle's attention step on the GPU's own set (it differs inside the band)
+                ref_o, ref_l = O.sparse_attention_row(host["q_attn"][b, t], host["kv"][b], sel, cfg.softmax_scale,
+                                                      cfg.v_dim)
+            assert np.abs(np64(out[b, 0]) - ref_o).max() <= tol, f"step {t} seq {b}"
+            assert np.abs(lse[b, 0].cpu().numpy() - ref_l).max() <= tol, f"step {t} seq {b}"

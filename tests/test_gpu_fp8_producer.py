@@ -107,10 +107,16 @@ def test_fp8_indexer_and_forward_from_produced_vectors(kw):
                          host["q_attn"], host["kv"], rows, cfg8.q_len, cfg8.topk, cfg8.softmax_scale, cfg8.v_dim)
     for (b, i), r in zip(rows, ref):
         n = O.visible_count(cfg8.q_len, cfg8.kv_len, i)
-        ok, swaps, msg = O.topk_band_check(r["scores"], idx[b, i].cpu().numpy(), n, cfg8.topk)
+        sel = idx[b, i].cpu().numpy()
+        ok, swaps, msg = O.topk_band_check(r["scores"], sel, n, cfg8.topk)
         assert ok, f"row {(b, i)}: {msg}"
-        assert np.abs(np64(out[b, i]) - r["out"]).max() <= 2e-2
-        assert np.abs(lse[b, i].cpu().numpy() - r["lse"]).max() <= 2e-2
+        ref_o, ref_l = r["out"], r["lse"]
+        if swaps:
+            # the oracle's attention step on the GPU's own set (it differs inside the band)
+            ref_o, ref_l = O.sparse_attention_row(host["q_attn"][b, i], host["kv"][b], sel, cfg8.softmax_scale,
+                                                  cfg8.v_dim)
+        assert np.abs(np64(out[b, i]) - ref_o).max() <= 2e-2
+        assert np.abs(lse[b, i].cpu().numpy() - ref_l).max() <= 2e-2
     # and the rotation kept the scores: FP8 scores from rotated vectors track
     # the bf16 scores of the unrotated activations
     qf = inp["q_idx"].float().cpu().numpy().astype(np.float64)
