@@ -45,7 +45,7 @@
 extern "C" {
 #endif
 
-#define DSA_ABI_VERSION 2
+#define DSA_ABI_VERSION 3
 
 typedef enum {
   DSA_OK = 0,
@@ -125,6 +125,17 @@ dsa_status_t dsa_index_scores(const dsa_problem_t* prob,
  */
 dsa_status_t dsa_topk(const dsa_problem_t* prob, const float* scores, int64_t row_stride,
                       int32_t* topk_idx, hipStream_t stream);
+
+/* Step 2 with a workspace: the same result as dsa_topk, bit for bit.
+ *   With few rows (B*Lq <= 128) of at least 4096 positions and more than K,
+ *   each row is cut into slices of 1024-4096 positions, one work-group per
+ *   slice, instead of one work-group per row; this needs
+ *   dsa_workspace_size(prob, DSA_OP_TOPK) bytes of workspace (16-byte
+ *   aligned).  When that size is 0 the call is dsa_topk (workspace may be
+ *   NULL).  Too small a workspace: DSA_ERR_WORKSPACE_TOO_SMALL.
+ */
+dsa_status_t dsa_topk_ws(const dsa_problem_t* prob, const float* scores, int64_t row_stride,
+                         int32_t* topk_idx, void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* Step 3: sparse MLA attention over the chosen rows (absorbed MQA form).
  *   q_attn   [B][Lq][NH][Dqk] attn_dtype
@@ -267,9 +278,11 @@ dsa_status_t dsa_out_unabsorb(const dsa_problem_t* prob, int32_t v_head_dim, con
 
 #define DSA_OP_ATTN 1
 #define DSA_OP_FORWARD 2
-/* Workspace bytes needed by dsa_sparse_mla_attn (op = DSA_OP_ATTN) or
- * dsa_forward (op = DSA_OP_FORWARD) for this problem; 0 for an invalid
- * problem or op.  Pure host function, no HIP call. */
+#define DSA_OP_TOPK 3
+/* Workspace bytes needed by dsa_sparse_mla_attn (op = DSA_OP_ATTN),
+ * dsa_forward (op = DSA_OP_FORWARD) or dsa_topk_ws (op = DSA_OP_TOPK) for
+ * this problem; 0 for an invalid problem or op.  Pure host function, no HIP
+ * call. */
 size_t dsa_workspace_size(const dsa_problem_t* prob, int32_t op);
 
 /* Number of query chunks dsa_forward splits this problem into (host only). */

@@ -8,5 +8,5 @@ from .dsa import (  # noqa: F401
     index_rotate_quantize, index_q_proj, head_weights_proj, head_weights_workspace_size, out_unabsorb,
     index_scores, lib,
     make_problem, sparse_mla_attn, status_string, topk, workspace_size,
-    DSA_OP_ATTN, DSA_OP_FORWARD, DSA_NUM_STAGES, STAGE_NAMES, DSA_F32, DSA_BF16, DSA_FP8_E4M3,
+    DSA_OP_ATTN, DSA_OP_FORWARD, DSA_OP_TOPK, DSA_NUM_STAGES, STAGE_NAMES, DSA_F32, DSA_BF16, DSA_FP8_E4M3,
 )

@@ -75,7 +75,7 @@ size_t attn_partials_bytes(const dsa_problem_t& p, int rows, int splits) {
 struct ForwardPlan {
   int chunk;       // queries per chunk
   int n_chunks;
-  int tk_slices, tk_slice_len;   // two-stage top-k (tk_slices > 1)
+  int tk_sl_len;                 // sliced top-k: positions per work-group (0 = not used)
   size_t scores_bytes, idx_bytes, part_bytes, cand_bytes;
   size_t total() const { return scores_bytes + idx_bytes + part_bytes + cand_bytes; }
 };
@@ -88,10 +88,28 @@ ForwardPlan plan_forward(const dsa_problem_t& p, Path path, bool need_idx) {
   f.idx_bytes = need_idx ? align_up((size_t)p.batch * p.q_len * p.topk * 4) : 0;
   const int rows = p.batch * f.chunk;
   f.part_bytes = attn_partials_bytes(p, rows, attn_splits(p, path, rows));
-  f.tk_slices = topk_slices(rows, p.kv_len, p.topk, &f.tk_slice_len);
-  // candidate positions and their scores
-  f.cand_bytes = f.tk_slices > 1 ? 2 * align_up((size_t)rows * f.tk_slices * p.topk * 4) : 0;
+  // few decode-shaped rows (the decode indexer kernel zeroes the histogram
+  // the sliced selection accumulates into): one work-group per row slice
+  f.tk_sl_len = (path != kPathF32 && f.chunk <= 4) ? topk_sliced_len(rows, p.kv_len, p.topk) : 0;
+  f.cand_bytes = 0;
+  if (f.tk_sl_len > 0) {
+    size_t hist_bytes;
+    f.cand_bytes = align_up(topk_sliced_bytes(rows, p.kv_len, f.tk_sl_len, &hist_bytes));
+  }
   return f;
+}
+
+// Workspace pieces of the sliced top-k, in the order topk_sliced_bytes counts them.
+void carve_sliced(TopkLaunch& ta, char* base, int rows, int n_max, int L) {
+  size_t hist_bytes;
+  topk_sliced_bytes(rows, n_max, L, &hist_bytes);
+  ta.sl_len = L;
+  ta.sl_count = (n_max + L - 1) / L;
+  ta.sl_hist = reinterpret_cast<uint32_t*>(base);
+  ta.sl_info = reinterpret_cast<int32_t*>(base + hist_bytes);
+  ta.sl_rowinfo = ta.sl_info + (size_t)rows * kMaxTopkSlices * 2;
+  ta.sl_list = reinterpret_cast<uint32_t*>(ta.sl_rowinfo + (size_t)rows * 4);
+  ta.sl_cand = ta.sl_list + (size_t)rows * ta.sl_count * L * 2;
 }
 
 IndexLaunch make_index(const dsa_problem_t& p, const void* q, const uint8_t* qs, const void* k, const uint8_t* ks,
@@ -102,6 +120,7 @@ IndexLaunch make_index(const dsa_problem_t& p, const void* q, const uint8_t* qs,
   a.B = p.batch; a.Lq = p.q_len; a.Lk = p.kv_len; a.H = p.index_heads; a.D = p.index_dim;
   a.Lc = p.kv_capacity ? p.kv_capacity : p.kv_len;
   a.q_begin = q_begin; a.q_count = q_count; a.write_masked = masked;
+  a.zero_hist = nullptr;
   return a;
 }
 
@@ -112,7 +131,8 @@ TopkLaunch make_topk(const dsa_problem_t& p, const float* scores, int64_t row_st
   a.B = p.batch; a.Lq = p.q_len; a.Lk = p.kv_len; a.K = p.topk;
   a.q_begin = q_begin; a.q_count = q_count;
   a.vec_ok = aligned16(scores) && (row_stride % 4) == 0;
-  a.slices = 1; a.slice_len = 0; a.cand = nullptr; a.cand_score = nullptr;
+  a.sl_len = 0; a.sl_count = 0; a.sl_hist = nullptr; a.sl_info = nullptr; a.sl_rowinfo = nullptr;
+  a.sl_list = nullptr; a.sl_cand = nullptr;
   return a;
 }
 
@@ -196,18 +216,17 @@ dsa_status_t forward_impl(const dsa_problem_t* prob, const void* q_idx, const ui
     // 1. scores for this chunk's rows (causal part only)
     if ((e = ev.rec(c, 0, 0)) != hipSuccess) return DSA_ERR_HIP;
     IndexLaunch ia = make_index(p, q_idx, q_scale, k_idx, k_scale, head_w, scores, p.kv_len, q0, qn, 0);
+    TopkLaunch ta = make_topk(p, scores, p.kv_len, idx, q0, qn);
+    if (f.tk_sl_len > 0) {
+      carve_sliced(ta, reinterpret_cast<char*>(cand), p.batch * f.chunk, p.kv_len, f.tk_sl_len);
+      ia.zero_hist = ta.sl_hist;
+    }
     if ((e = run_index(path, ia, stream)) != hipSuccess) return hip_status(e);
     if ((e = ev.rec(c, 0, 1)) != hipSuccess) return DSA_ERR_HIP;
     // 2. top-k
     if ((e = ev.rec(c, 1, 0)) != hipSuccess) return DSA_ERR_HIP;
-    TopkLaunch ta = make_topk(p, scores, p.kv_len, idx, q0, qn);
-    if (f.tk_slices > 1) {
-      ta.slices = f.tk_slices;
-      ta.slice_len = f.tk_slice_len;
-      ta.cand = cand;
-      ta.cand_score = reinterpret_cast<float*>(reinterpret_cast<char*>(cand) + f.cand_bytes / 2);
-    }
-    if ((e = launch_topk(ta, stream)) != hipSuccess) return hip_status(e);
+    e = f.tk_sl_len > 0 ? launch_topk_sliced(ta, false, stream) : launch_topk(ta, stream);
+    if (e != hipSuccess) return hip_status(e);
     if ((e = ev.rec(c, 1, 1)) != hipSuccess) return DSA_ERR_HIP;
     // 3. attention (+ combine); every chunk uses the split count the
     //    workspace was sized for (that of a full chunk)
@@ -278,6 +297,26 @@ dsa_status_t dsa_topk(const dsa_problem_t* prob, const float* scores, int64_t ro
   return hip_status(launch_topk(make_topk(*prob, scores, row_stride, topk_idx, 0, prob->q_len), stream));
 }
 
+dsa_status_t dsa_topk_ws(const dsa_problem_t* prob, const float* scores, int64_t row_stride, int32_t* topk_idx,
+                         void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  Path path;
+  dsa_status_t st = check_problem(prob, &path);
+  if (st != DSA_OK) return st;
+  if (!scores || !topk_idx || row_stride < prob->kv_len) return DSA_ERR_INVALID_ARGUMENT;
+  if ((reinterpret_cast<uintptr_t>(scores) & 3u) || (reinterpret_cast<uintptr_t>(topk_idx) & 3u))
+    return DSA_ERR_INVALID_ARGUMENT;
+  const dsa_problem_t& p = *prob;
+  TopkLaunch ta = make_topk(p, scores, row_stride, topk_idx, 0, p.q_len);
+  const int rows = p.batch * p.q_len;
+  const int L = topk_sliced_len(rows, p.kv_len, p.topk);
+  if (L == 0) return hip_status(launch_topk(ta, stream));
+  size_t hist_bytes;
+  if (workspace_bytes < topk_sliced_bytes(rows, p.kv_len, L, &hist_bytes)) return DSA_ERR_WORKSPACE_TOO_SMALL;
+  if (!workspace || !aligned16(workspace)) return DSA_ERR_INVALID_ARGUMENT;
+  carve_sliced(ta, static_cast<char*>(workspace), rows, p.kv_len, L);
+  return hip_status(launch_topk_sliced(ta, true, stream));
+}
+
 dsa_status_t dsa_sparse_mla_attn(const dsa_problem_t* prob, const void* q_attn, const void* kv,
                                  const int32_t* topk_idx, void* out, float* lse, void* workspace,
                                  size_t workspace_bytes, hipStream_t stream) {
@@ -330,6 +369,12 @@ size_t dsa_workspace_size(const dsa_problem_t* prob, int32_t op) {
   if (op == DSA_OP_FORWARD) {
     const ForwardPlan f = plan_forward(p, path, true);
     return f.total();
+  }
+  if (op == DSA_OP_TOPK) {
+    const int rows = p.batch * p.q_len;
+    const int L = topk_sliced_len(rows, p.kv_len, p.topk);
+    size_t hist_bytes;
+    return L == 0 ? 0 : topk_sliced_bytes(rows, p.kv_len, L, &hist_bytes);
   }
   return 0;
 }

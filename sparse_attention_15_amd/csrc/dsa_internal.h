@@ -21,6 +21,8 @@ struct IndexLaunch {
   int Lc;                  // tokens per sequence in the key caches (>= Lk)
   int q_begin, q_count;
   int write_masked;        // also write -inf for positions beyond the causal limit
+  uint32_t* zero_hist;     // decode shape only: rows x kTopkRowHeadWords words set to
+                           // zero for the sliced top-k that follows (null: none)
 };
 
 struct TopkLaunch {
@@ -30,14 +32,23 @@ struct TopkLaunch {
   int B, Lq, Lk, K;
   int q_begin, q_count;
   int vec_ok;              // rows are 16-byte aligned: use 16-byte loads
-  // two-stage selection (slices > 1): each row's slices of slice_len
-  // positions first keep their own top K in cand [rows][slices][K]
-  // (positions, -1 for none) with their scores in cand_score (same shape),
-  // which the second stage reads in place of gathering them
-  int slices, slice_len;
-  int32_t* cand;
-  float* cand_score;
+  // sliced selection (launch_topk_sliced): rows cut into sl_count slices of
+  // sl_len positions, one work-group each; workspace per row: a 4096-bin
+  // histogram (zero on entry), per-slice counts [kMaxTopkSlices][2], the
+  // row's threshold bin [4], per-slice kept lists of (key, position) and
+  // per-slice candidate keys (those in the threshold bin)
+  int sl_len, sl_count;
+  uint32_t* sl_hist;
+  int32_t* sl_info;
+  int32_t* sl_rowinfo;
+  uint32_t* sl_list;
+  uint32_t* sl_cand;
 };
+
+constexpr int kMaxTopkSlices = 512;
+// Per-row head of the sliced top-k workspace, zero when a selection starts:
+// a 4096-bin histogram followed by the row's barrier counters.
+constexpr int kTopkRowHeadWords = 4096 + 64;
 
 struct AttnLaunch {
   const void* qa;          // [B][Lq][NH][Dqk]
@@ -76,9 +87,14 @@ hipError_t launch_rotate_quant(const void* x, int f32_in, int64_t rows, uint8_t*
 
 // Top-k (all dtypes: scores are fp32).
 hipError_t launch_topk(const TopkLaunch& a, hipStream_t s);
-// Slices per row for a two-stage selection over `rows` rows of up to n_max
-// positions (1 = single stage); writes the slice length.
-int topk_slices(int rows, int n_max, int K, int* slice_len);
+// Sliced top-k for few long rows: slice length (1024, 2048 or 4096) for
+// `rows` rows of up to n_max positions, or 0 when one work-group per row
+// is the better plan; workspace bytes of that plan (and of its histogram,
+// which must be zero when the selection starts).
+int topk_sliced_len(int rows, int n_max, int K);
+size_t topk_sliced_bytes(int rows, int n_max, int L, size_t* hist_bytes);
+// zero_hist: clear the histogram first (else the caller's earlier kernel did).
+hipError_t launch_topk_sliced(const TopkLaunch& a, bool zero_hist, hipStream_t s);
 
 // Sparse MLA.  *_bf16 needs NH = 128, Dqk = 576, Dv = 512.
 hipError_t launch_attn_f32(const AttnLaunch& a, hipStream_t s);

@@ -233,6 +233,11 @@ __global__ __launch_bounds__(256, 2) void idx_decode_kernel(IndexLaunch a) {
     for (int s = max(c0, n) + tid; s < c1; s += 256) out[s] = kNegInf;
     wait_vmcnt<0>();
   }
+  if (a.zero_hist && blockIdx.x == 0) {          // the sliced top-k's row head
+    u32x4* h = reinterpret_cast<u32x4*>(a.zero_hist + (int64_t)row * kTopkRowHeadWords);
+    for (int j = tid; j < kTopkRowHeadWords / 4; j += 256) h[j] = u32x4{0u, 0u, 0u, 0u};
+    wait_vmcnt<0>();
+  }
   if (c0 >= cn) return;                          // uniform over the work-group
   const int nk = cn - c0;
   const int ntile = (nk + TK - 1) / TK;

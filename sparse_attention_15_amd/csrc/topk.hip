@@ -154,62 +154,24 @@ __device__ void find_bin(Shared<NC, C>& sh, const uint32_t* h, int nb, uint32_t 
   __syncthreads();
 }
 
-// Modes: kRows selects from score rows; kSlice (first of two stages for a
-// few long rows) selects the top K of each slice of a row into a candidate
-// list (positions, and the scores beside them); kCand (second stage)
-// selects from a row's candidate lists, reading their scores in order.
-enum { kRows = 0, kSlice = 1, kCand = 2 };
-
 // NC 16-byte chunks per thread kept in registers (0 = re-read each pass);
 // C histogram copies.
-template <int NC, int C, int MODE>
+template <int NC, int C>
 __global__ __launch_bounds__(kThreads, NC == 2 ? 8 : 4) void topk_kernel(TopkLaunch a) {
   __shared__ Shared<NC, C> sh;
   constexpr int S = Shared<NC, C>::kStride;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int r = gridDim.x - 1 - blockIdx.x;       // longest rows first
-  const int row = MODE == kSlice ? r / a.slices : r;
-  const int slice = MODE == kSlice ? r - row * a.slices : 0;
+  const int row = r;
   const int b = row / a.q_count;
   const int i = a.q_begin + row % a.q_count;
   const int n_row = a.Lk - a.Lq + i + 1;          // visible keys of this query
   const int K = a.K;
   const float* src = a.scores + (int64_t)row * a.row_stride;
-  const int p0 = slice * a.slice_len;             // first position of the slice
-  int n;                                          // elements to select from
-  int32_t* out;
-  float* out_score = nullptr;                     // kSlice: the kept candidates' scores
-  const int32_t* cand = nullptr;                  // kCand: this row's candidate positions
-  if constexpr (MODE == kRows) {
-    n = n_row;
-    out = a.out + ((int64_t)b * a.Lq + i) * K;
-  } else if constexpr (MODE == kSlice) {
-    n = max(0, min(a.slice_len, n_row - p0));
-    src += p0;
-    out = a.cand + ((int64_t)row * a.slices + slice) * K;
-    out_score = a.cand_score + ((int64_t)row * a.slices + slice) * K;
-  } else {
-    n = a.slices * K;
-    cand = a.cand + (int64_t)row * a.slices * K;
-    src = a.cand_score + (int64_t)row * a.slices * K;   // element x's score
-    out = a.out + ((int64_t)b * a.Lq + i) * K;
-  }
-  // position of element x of this selection in the row
-  auto pos_of = [&](int x) -> int32_t {
-    if constexpr (MODE == kSlice) return p0 + x;
-    else if constexpr (MODE == kCand) return cand[x];
-    else return x;
-  };
-
-  if (MODE == kCand && n_row <= K) {             // the whole row is chosen
-    for (int j = tid; j < K; j += kThreads) out[j] = j < n_row ? j : -1;
-    return;
-  }
-  if (n <= K) {                                   // kCand never: n = slices * K > K
-    for (int j = tid; j < K; j += kThreads) {
-      out[j] = j < n ? pos_of(j) : -1;
-      if constexpr (MODE == kSlice) out_score[j] = j < n ? src[j] : 0.f;
-    }
+  const int n = n_row;                            // elements to select from
+  int32_t* out = a.out + ((int64_t)b * a.Lq + i) * K;
+  if (n <= K) {                                   // every visible position, then -1
+    for (int j = tid; j < K; j += kThreads) out[j] = j < n ? j : -1;
     return;
   }
   const int nchunks = (n + 3) >> 2;               // 4 positions per chunk
@@ -218,31 +180,15 @@ __global__ __launch_bounds__(kThreads, NC == 2 ? 8 : 4) void topk_kernel(TopkLau
   auto load_keys = [&](int c, uint32_t (&kk)[4]) {
     const int ch = c * kThreads + tid;
     const int pos = ch * 4;
-    if constexpr (MODE == kCand) {
-      // candidates: a position, or -1 for an unused slot (key 0: never chosen)
-      if (a.vec_ok && pos + 3 < n) {
-        const u32x4 cv = ld16(cand + pos);
-        const f32x4 sv = *reinterpret_cast<const f32x4*>(src + pos);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) kk[e] = (int32_t)cv[e] >= 0 ? order_key(sv[e]) : 0u;
-      } else {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int32_t cx = pos + e < n ? cand[pos + e] : -1;
-          kk[e] = cx >= 0 ? order_key(src[pos + e]) : 0u;
-        }
-      }
+    if (a.vec_ok && pos + 3 < n) {
+      const f32x4 v = *reinterpret_cast<const f32x4*>(src + pos);
+      kk[0] = order_key(v.x);
+      kk[1] = order_key(v.y);
+      kk[2] = order_key(v.z);
+      kk[3] = order_key(v.w);
     } else {
-      if (a.vec_ok && pos + 3 < n) {
-        const f32x4 v = *reinterpret_cast<const f32x4*>(src + pos);
-        kk[0] = order_key(v.x);
-        kk[1] = order_key(v.y);
-        kk[2] = order_key(v.z);
-        kk[3] = order_key(v.w);
-      } else {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) kk[e] = (pos + e < n) ? order_key(src[pos + e]) : 0u;
-      }
+      for (int e = 0; e < 4; ++e) kk[e] = (pos + e < n) ? order_key(src[pos + e]) : 0u;
     }
   };
 
@@ -258,27 +204,17 @@ __global__ __launch_bounds__(kThreads, NC == 2 ? 8 : 4) void topk_kernel(TopkLau
     const int cfull = a.vec_ok ? n / (4 * kThreads) : 0;
     const int crag = cfull < iters ? cfull : NC;  // the chunk loaded lane by lane
     auto inside = [&](int c, int e) { return c < cfull || (c < iters && (c * kThreads + tid) * 4 + e < n); };
-    if (a.vec_ok && NC >= 8 && (MODE != kCand || NC <= 8)) {
-      // src: the row's scores, or (kCand) the candidates' scores in order
+    if (a.vec_ok && NC >= 8) {
       float vr[4] = {0.f, 0.f, 0.f, 0.f};        // the ragged chunk
-      int32_t ar[4] = {-1, -1, -1, -1};
       const int rpos = (crag * kThreads + tid) * 4;
       if (crag < NC) {                            // lanes wholly inside still take one load
         if (rpos + 3 < n) {
           const f32x4 t = *reinterpret_cast<const f32x4*>(src + rpos);
 #pragma unroll
           for (int e = 0; e < 4; ++e) vr[e] = t[e];
-          if constexpr (MODE == kCand) {
-            const u32x4 cv = ld16(cand + rpos);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) ar[e] = (int32_t)cv[e];
-          }
         } else {
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            vr[e] = rpos + e < n ? src[rpos + e] : 0.f;
-            if constexpr (MODE == kCand) ar[e] = rpos + e < n ? cand[rpos + e] : -1;
-          }
+          for (int e = 0; e < 4; ++e) vr[e] = rpos + e < n ? src[rpos + e] : 0.f;
         }
       }
       float v[NC][4];
@@ -290,32 +226,15 @@ __global__ __launch_bounds__(kThreads, NC == 2 ? 8 : 4) void topk_kernel(TopkLau
         v[c][2] = t.z;
         v[c][3] = t.w;
       }
-      if constexpr (MODE == kCand) {
-        // a candidate slot holds a position, or -1 for none (key 0)
-        int32_t at[NC][4];
 #pragma unroll
-        for (int c = 0; c < NC; ++c) {
-          const u32x4 cv = ld16(cand + (c < cfull ? (c * kThreads + tid) * 4 : 0));
+      for (int c = 0; c < NC; ++c)
 #pragma unroll
-          for (int e = 0; e < 4; ++e) at[c][e] = c < cfull ? (int32_t)cv[e] : (c == crag ? ar[e] : -1);
-        }
-#pragma unroll
-        for (int c = 0; c < NC; ++c)
-#pragma unroll
-          for (int e = 0; e < 4; ++e)
-            keys[c][e] = at[c][e] >= 0 ? order_key(c < cfull ? v[c][e] : vr[e]) : 0u;
-      } else {
-#pragma unroll
-        for (int c = 0; c < NC; ++c)
-#pragma unroll
-          for (int e = 0; e < 4; ++e)
-            keys[c][e] = inside(c, e) ? order_key(c < cfull ? v[c][e] : vr[e]) : 0u;
-      }
+        for (int e = 0; e < 4; ++e)
+          keys[c][e] = inside(c, e) ? order_key(c < cfull ? v[c][e] : vr[e]) : 0u;
     } else {
-      // unaligned rows, short rows (one or two chunks: nothing to overlap,
-      // and masked extra loads cost more than they hide), and the widest
-      // candidate lists (positions and scores would not fit the registers
-      // at once): chunk by chunk
+      // unaligned rows and short rows (one or two chunks: nothing to
+      // overlap, and masked extra loads cost more than they hide): chunk by
+      // chunk
 #pragma unroll
       for (int c = 0; c < NC; ++c) {
         if (c < iters) load_keys(c, keys[c]);
@@ -346,13 +265,11 @@ __global__ __launch_bounds__(kThreads, NC == 2 ? 8 : 4) void topk_kernel(TopkLau
   if (tid < 64) st16(&sh.h3[4 * tid], u32x4{0u, 0u, 0u, 0u});
   __syncthreads();
   {
-    constexpr bool kEvery = MODE != kCand;
     auto count1 = [&](const uint32_t (&kk)[4]) {
 #pragma unroll
-      for (int e = 0; e < 4; ++e)
-        if (kEvery || kk[e] != 0u) atomicAdd(&sh.hist[copy_base + (kk[e] >> 20)], 1u);
+      for (int e = 0; e < 4; ++e) atomicAdd(&sh.hist[copy_base + (kk[e] >> 20)], 1u);
     };
-    if (kEvery && tid == 0 && pad != 0u) atomicSub(&sh.hist[0], pad);
+    if (tid == 0 && pad != 0u) atomicSub(&sh.hist[0], pad);
     if constexpr (NC > 0) {
 #pragma unroll
       for (int c = 0; c < NC; ++c)
@@ -417,7 +334,6 @@ __global__ __launch_bounds__(kThreads, NC == 2 ? 8 : 4) void topk_kernel(TopkLau
         sh.hist[slot] = (uint32_t)pos;
       } else {
         out[slot] = pos;
-        if constexpr (MODE == kSlice) out_score[slot] = src[pos - p0];
       }
     }
   };
@@ -510,7 +426,7 @@ __global__ __launch_bounds__(kThreads, NC == 2 ? 8 : 4) void topk_kernel(TopkLau
         }
         const int base = 32 * (tid * J + j);
         while (sel != 0u) {
-          put(slot++, pos_of(base + __builtin_ctz(sel)));
+          put(slot++, base + __builtin_ctz(sel));
           sel &= sel - 1u;
         }
         g_b += __builtin_popcount(gw[j]);
@@ -569,7 +485,7 @@ __global__ __launch_bounds__(kThreads, NC == 2 ? 8 : 4) void topk_kernel(TopkLau
             const uint32_t m = kk[g][e] & mask;
             const bool valid = kk[g][e] != 0u;
             const bool gt = valid && m > prefix, eq = valid && m == prefix;
-            if (gt || (eq && e_b < k_rem)) put(g_b + min(e_b, k_rem), pos_of(pos0 + e));
+            if (gt || (eq && e_b < k_rem)) put(g_b + min(e_b, k_rem), pos0 + e);
             g_b += gt ? 1u : 0u;
             e_b += eq ? 1u : 0u;
           }
@@ -596,9 +512,6 @@ __global__ __launch_bounds__(kThreads, NC == 2 ? 8 : 4) void topk_kernel(TopkLau
     } else {
       for (int j = tid; j < K; j += kThreads) out[j] = (int32_t)sh.hist[j];
     }
-    // the kept candidates' scores, re-read from the slice (just loaded)
-    if constexpr (MODE == kSlice)
-      for (int j = tid; j < K; j += kThreads) out_score[j] = src[(int)sh.hist[j] - p0];
   }
 }
 
@@ -606,55 +519,27 @@ __global__ __launch_bounds__(kThreads, NC == 2 ? 8 : 4) void topk_kernel(TopkLau
 
 namespace {
 
-template <int MODE>
-void launch_mode(const TopkLaunch& a, int n_max, int grid, hipStream_t s) {
+void launch_rows(const TopkLaunch& a, int n_max, int grid, hipStream_t s) {
   const int chunks = (n_max + 3) / 4;
   const int iters = (chunks + kThreads - 1) / kThreads;
   // short rows come in large numbers (prefill): small histograms keep two
   // work-groups per CU; long rows are few and get the widest spreading
   if (iters <= 2)
-    hipLaunchKernelGGL((topk_kernel<2, 2, MODE>), dim3(grid), dim3(kThreads), 0, s, a);
+    hipLaunchKernelGGL((topk_kernel<2, 2>), dim3(grid), dim3(kThreads), 0, s, a);
   else if (iters <= 8)
-    hipLaunchKernelGGL((topk_kernel<8, 8, MODE>), dim3(grid), dim3(kThreads), 0, s, a);
+    hipLaunchKernelGGL((topk_kernel<8, 8>), dim3(grid), dim3(kThreads), 0, s, a);
   else if (iters <= 16)
-    hipLaunchKernelGGL((topk_kernel<16, 8, MODE>), dim3(grid), dim3(kThreads), 0, s, a);
-  else if constexpr (MODE != kCand)              // candidate rows are at most 65536 long
-    hipLaunchKernelGGL((topk_kernel<0, 8, MODE>), dim3(grid), dim3(kThreads), 0, s, a);
+    hipLaunchKernelGGL((topk_kernel<16, 8>), dim3(grid), dim3(kThreads), 0, s, a);
+  else
+    hipLaunchKernelGGL((topk_kernel<0, 8>), dim3(grid), dim3(kThreads), 0, s, a);
 }
 
 }  // namespace
 
-int topk_slices(int rows, int n_max, int K, int* slice_len) {
-  *slice_len = 0;
-  // one work-group per row keeps one CU's VALU busy over the whole row; with
-  // fewer rows than CUs, split long rows into slices of about sqrt(n K) / 2
-  // positions (more, shorter slices: the second stage reads its candidates'
-  // scores in order, so it costs little more per candidate than the first
-  // per position).  Each stage has a fixed cost of a few microseconds
-  // (passes, barriers), so rows below 65536 positions stay single-stage
-  // (measured: 32768-position decode rows take 15.6 us in one stage, 20.2
-  // us in two with 8 slices of 4096 and 23.9 with 4 of 8192).
-  // 131072-position rows: 82 us in one stage; in two, 27.1 us
-  // with 8 slices of 16384, 25.3 us with 4 of 32768, 25.1 us with 16 of
-  // 8192.
-  if (rows >= 256 || K > 4096 || (K & 3) || n_max < 4 * K || n_max < 65536) return 1;
-  int len = 4096;
-  while (4 * (int64_t)len * len < (int64_t)n_max * K) len *= 2;
-  const int sl = (n_max + len - 1) / len;
-  if (sl < 2 || (int64_t)sl * K > 65536) return 1;
-  *slice_len = len;
-  return sl;
-}
-
 hipError_t launch_topk(const TopkLaunch& a, hipStream_t s) {
   const int rows = a.B * a.q_count;
   const int n_max = a.Lk - a.Lq + a.q_begin + a.q_count;
-  if (a.slices > 1) {
-    launch_mode<kSlice>(a, a.slice_len, rows * a.slices, s);
-    launch_mode<kCand>(a, a.slices * a.K, rows, s);
-  } else {
-    launch_mode<kRows>(a, n_max, rows, s);
-  }
+  launch_rows(a, n_max, rows, s);
   return hipGetLastError();
 }
 

@@ -19,7 +19,7 @@ LIB_PATH = os.path.join(_HERE, "libdsa.so")
 
 DSA_OK, DSA_ERR_INVALID_ARGUMENT, DSA_ERR_UNSUPPORTED, DSA_ERR_WORKSPACE_TOO_SMALL, DSA_ERR_HIP = range(5)
 DSA_F32, DSA_BF16, DSA_FP8_E4M3 = 0, 1, 2
-DSA_OP_ATTN, DSA_OP_FORWARD = 1, 2
+DSA_OP_ATTN, DSA_OP_FORWARD, DSA_OP_TOPK = 1, 2, 3
 DSA_NUM_STAGES = 4
 STAGE_NAMES = ("indexer", "topk", "attention", "combine")
 
@@ -60,6 +60,7 @@ def lib() -> ctypes.CDLL:
     sigs = {
         "dsa_index_scores": [P, V, V, V, V, V, V, V],
         "dsa_topk": [P, V, I64, V, V],
+        "dsa_topk_ws": [P, V, I64, V, V, SZ, V],
         "dsa_sparse_mla_attn": [P, V, V, V, V, V, V, SZ, V],
         "dsa_forward": [P, V, V, V, V, V, V, V, V, V, V, V, SZ, V],
         "dsa_forward_timed": [P, V, V, V, V, V, V, V, V, V, V, V, SZ, V, I32, V, V],
@@ -184,10 +185,12 @@ def index_scores(p: Problem, q_idx, q_scale, k_idx, k_scale, head_w, scores=None
     return scores
 
 
-def topk(p: Problem, scores, out=None) -> torch.Tensor:
+def topk(p: Problem, scores, out=None, workspace=None) -> torch.Tensor:
     """[B, Lq, K] int32 positions (ascending, -1 padded) from fp32 score rows.
 
     scores: [B, Lq, S] with S >= Lk (row stride S); only the causal prefix is read.
+    workspace: None (dsa_topk: one work-group per row), "auto" or a uint8
+    device tensor (dsa_topk_ws: few long rows spread over work-groups per slice).
     """
     if scores.dim() != 3 or scores.shape[0] != p.batch or scores.shape[1] != p.q_len:
         raise ValueError(f"scores: shape {tuple(scores.shape)}")
@@ -195,7 +198,12 @@ def topk(p: Problem, scores, out=None) -> torch.Tensor:
         out = torch.empty(p.batch, p.q_len, p.topk, dtype=torch.int32, device=scores.device)
     sp = _ptr(scores, "scores", torch.float32)
     op = _ptr(out, "topk_idx", torch.int32, (p.batch, p.q_len, p.topk))
-    _check(lib().dsa_topk(ctypes.byref(p), sp, scores.shape[2], op, _stream()), "dsa_topk")
+    if workspace is None:
+        _check(lib().dsa_topk(ctypes.byref(p), sp, scores.shape[2], op, _stream()), "dsa_topk")
+        return out
+    ws = _workspace(p, DSA_OP_TOPK, None if isinstance(workspace, str) else workspace, scores.device)
+    _check(lib().dsa_topk_ws(ctypes.byref(p), sp, scores.shape[2], op, ctypes.c_void_p(ws.data_ptr()),
+                             ws.numel(), _stream()), "dsa_topk_ws")
     return out
 
 

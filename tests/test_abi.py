@@ -37,7 +37,7 @@ def test_library_exports_every_declared_symbol(dsa):
     L = dsa.lib()
     for name in _declared_functions():
         assert hasattr(L, name), name
-    assert dsa.abi_version() == 2
+    assert dsa.abi_version() == 3
 
 
 def test_status_strings(dsa):
@@ -154,3 +154,33 @@ def test_cache_append_checks_capacity_without_launching(dsa):
     assert _call_forward(dsa, small) == dsa.DSA_ERR_INVALID_ARGUMENT
     room = dsa.make_problem(C.DECODE_32K, kv_capacity=40000)
     assert L.dsa_cache_append(ctypes.byref(room), 4, v, None, None, v, None, v, None) == dsa.DSA_ERR_INVALID_ARGUMENT
+
+
+def test_sliced_topk_plan_is_host_only_and_bounded(dsa):
+    # few rows of 65536 positions or more get a workspace for the sliced
+    # selection; many rows, shorter rows, and rows of at most K positions
+    # select one work-group per row
+    p4 = dsa.make_problem(C.DECODE_128K)
+    need = dsa.workspace_size(p4, dsa.DSA_OP_TOPK)
+    assert need >= 8 * 131072 * 12                    # kept lists and candidates can hold every position
+    assert dsa.workspace_size(dsa.make_problem(C.DECODE_32K), dsa.DSA_OP_TOPK) == 0
+    assert dsa.workspace_size(dsa.make_problem(C.PREFILL_8K), dsa.DSA_OP_TOPK) == 0
+    assert dsa.workspace_size(_prob(dsa, C.DECODE_128K, batch=200), dsa.DSA_OP_TOPK) == 0
+    assert dsa.workspace_size(_prob(dsa, C.DECODE_128K, kv_len=65535), dsa.DSA_OP_TOPK) == 0
+    for batch, lk, k in ((1, 65536, 1), (8, 131072, 2048), (1, 1 << 21, 2048), (128, 70000, 4999), (3, 70001, 7)):
+        n = dsa.workspace_size(_prob(dsa, C.DECODE_128K, batch=batch, kv_len=lk, topk=k), dsa.DSA_OP_TOPK)
+        # row head + per-slice counts + row info + a (key, position) pair and a key per position
+        assert n >= batch * ((4096 + 64) * 4 + 512 * 8 + 16 + lk * 12), (batch, lk, k)
+        assert n <= batch * ((4096 + 64) * 4 + 512 * 8 + 16 + (lk + 4096) * 12), (batch, lk, k)
+    # the forward's workspace covers its sliced selection
+    assert dsa.workspace_size(p4, dsa.DSA_OP_FORWARD) >= need
+
+
+def test_topk_ws_rejects_small_workspace_before_launch(dsa):
+    L = dsa.lib()
+    p = dsa.make_problem(C.DECODE_128K)
+    v = ctypes.c_void_p(16)
+    need = dsa.workspace_size(p, dsa.DSA_OP_TOPK)
+    assert L.dsa_topk_ws(ctypes.byref(p), v, 131072, v, v, need - 1, None) == dsa.DSA_ERR_WORKSPACE_TOO_SMALL
+    assert L.dsa_topk_ws(ctypes.byref(p), v, 131072, v, None, need, None) == dsa.DSA_ERR_INVALID_ARGUMENT
+    assert L.dsa_topk_ws(ctypes.byref(p), v, 100, v, v, need, None) == dsa.DSA_ERR_INVALID_ARGUMENT
