@@ -45,7 +45,7 @@
 extern "C" {
 #endif
 
-#define DSA_ABI_VERSION 3
+#define DSA_ABI_VERSION 4
 
 typedef enum {
   DSA_OK = 0,
@@ -292,6 +292,12 @@ int32_t dsa_forward_chunks(const dsa_problem_t* prob);
  * dsa_forward's attention step (1: no split, no combine launch); 0 for an
  * invalid problem.  Host only. */
 int32_t dsa_forward_attn_splits(const dsa_problem_t* prob);
+
+/* Positions per work-group of the sliced top-k dsa_forward uses for this
+ * problem (1024, 2048 or 4096: each long decode row is cut into slices that
+ * several work-groups select from together), or 0 when each row is selected
+ * by one work-group (or the problem is invalid).  Host only. */
+int32_t dsa_forward_topk_slice_len(const dsa_problem_t* prob);
 
 /* Static description of a status code. */
 const char* dsa_status_string(dsa_status_t status);

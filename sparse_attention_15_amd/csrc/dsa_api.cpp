@@ -465,6 +465,12 @@ int32_t dsa_forward_attn_splits(const dsa_problem_t* prob) {
   return attn_splits(*prob, path, prob->batch * f.chunk);
 }
 
+int32_t dsa_forward_topk_slice_len(const dsa_problem_t* prob) {
+  Path path;
+  if (check_problem(prob, &path) != DSA_OK) return 0;
+  return plan_forward(*prob, path, true).tk_sl_len;
+}
+
 const char* dsa_status_string(dsa_status_t s) {
   switch (s) {
     case DSA_OK: return "ok";

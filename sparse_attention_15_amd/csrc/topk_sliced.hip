@@ -506,13 +506,15 @@ __global__ __launch_bounds__(kT) void tk_emit_kernel(TopkLaunch a, int L) {
 // atomics: histogram adds, and relaxed atomic stores and loads (which the
 // compiler issues with the system-coherent cache bit, so they complete at
 // and read from the device's coherence point rather than a per-XCD L2).
-// The barrier's work-group barrier waits for each wave's memory operations
-// to complete before the arrival is issued, and readers load only after
-// seeing every arrival, so no L2 write-back or invalidation is needed.
+// Each wave waits for its own stores and atomics to complete (a work-group
+// barrier alone does not) before the work-group barrier that precedes the
+// arrival, and readers load only after seeing every arrival, so no L2
+// write-back or invalidation is needed.
 constexpr int kSpinMax = 1 << 18;
 
 __device__ __forceinline__ void row_barrier(uint32_t* ctr, uint32_t target) {
-  __syncthreads();                               // every wave's stores and atomics have completed
+  wait_vmcnt<0>();                               // this wave's stores and atomics have completed
+  __syncthreads();                               // ... and every other wave's
   if (threadIdx.x == 0) {
     __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     for (int spin = 0; spin < kSpinMax; ++spin) {

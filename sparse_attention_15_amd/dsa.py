@@ -75,6 +75,8 @@ def lib() -> ctypes.CDLL:
     L.dsa_forward_chunks.restype = I32
     L.dsa_forward_attn_splits.argtypes = [P]
     L.dsa_forward_attn_splits.restype = I32
+    L.dsa_forward_topk_slice_len.argtypes = [P]
+    L.dsa_forward_topk_slice_len.restype = I32
     L.dsa_index_rotate_quantize.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_int32,
                                             ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
     L.dsa_index_rotate_quantize.restype = ctypes.c_int
@@ -217,6 +219,11 @@ def forward_chunks(p: Problem) -> int:
 
 def attn_splits(p: Problem) -> int:
     return int(lib().dsa_forward_attn_splits(ctypes.byref(p)))
+
+
+def topk_slice_len(p: Problem) -> int:
+    """Positions per work-group of forward's sliced top-k (0: one work-group per row)."""
+    return int(lib().dsa_forward_topk_slice_len(ctypes.byref(p)))
 
 
 def cache_append(p: Problem, k_new, k_new_scale, kv_new, k_idx, k_scale, kv):

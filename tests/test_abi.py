@@ -37,7 +37,7 @@ def test_library_exports_every_declared_symbol(dsa):
     L = dsa.lib()
     for name in _declared_functions():
         assert hasattr(L, name), name
-    assert dsa.abi_version() == 3
+    assert dsa.abi_version() == 4
 
 
 def test_status_strings(dsa):
@@ -174,6 +174,12 @@ def test_sliced_topk_plan_is_host_only_and_bounded(dsa):
         assert n <= batch * ((4096 + 64) * 4 + 512 * 8 + 16 + (lk + 4096) * 12), (batch, lk, k)
     # the forward's workspace covers its sliced selection
     assert dsa.workspace_size(p4, dsa.DSA_OP_FORWARD) >= need
+    # the forward's plan query names the same choice: 4096 positions per
+    # work-group for 8 rows of 128K (32 slices each), none for 32 rows of 32K
+    assert dsa.topk_slice_len(p4) == 4096
+    assert dsa.topk_slice_len(dsa.make_problem(C.DECODE_32K)) == 0
+    assert dsa.topk_slice_len(_prob(dsa, C.DECODE_128K, batch=1)) == 1024
+    assert dsa.topk_slice_len(_prob(dsa, C.DECODE_128K, q_len=0)) == 0
 
 
 def test_topk_ws_rejects_small_workspace_before_launch(dsa):
