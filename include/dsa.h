@@ -19,7 +19,9 @@
  *   - Every tensor pointer is a caller-owned DEVICE pointer to a contiguous
  *     row-major array with the layout given below, 16-byte aligned.  The
  *     library never allocates, frees or keeps memory; temporary memory comes
- *     from a caller workspace sized by dsa_workspace_size().
+ *     from a caller workspace sized by dsa_workspace_size().  The one
+ *     exception is dsa_forward_static, which works in a fixed device array
+ *     of the library (one per GPU) instead of a workspace.
  *   - Calls are asynchronous on `stream` (hipStream_t; 0 = the null stream):
  *     the caller keeps every buffer alive until the stream has passed the
  *     call.  No host synchronisation happens inside the library.
@@ -31,8 +33,9 @@
  *     keys 0..p (n = p + 1 of them): the causal mask keeps the diagonal
  *     (atlas token-ids page, transformer-forward excerpt), and a single decode
  *     query sees the whole cache.
- *   - The library keeps no mutable global state: calls on different streams
- *     or host threads are independent.
+ *   - The library keeps no mutable global state (dsa_forward_static's scratch
+ *     array aside): calls on different streams or host threads are
+ *     independent.
  */
 #ifndef DSA_H_
 #define DSA_H_
@@ -45,14 +48,16 @@
 extern "C" {
 #endif
 
-#define DSA_ABI_VERSION 4
+#define DSA_ABI_VERSION 5
 
 typedef enum {
   DSA_OK = 0,
   DSA_ERR_INVALID_ARGUMENT = 1,   /* null pointer, bad size, misalignment */
   DSA_ERR_UNSUPPORTED = 2,        /* valid request this build has no kernel for */
   DSA_ERR_WORKSPACE_TOO_SMALL = 3,
-  DSA_ERR_HIP = 4                 /* a HIP runtime call or launch failed */
+  DSA_ERR_HIP = 4,                /* a HIP runtime call or launch failed */
+  DSA_ERR_EXCEEDS_SCRATCH = 5     /* dsa_forward_static: the problem needs more
+                                     than DSA_STATIC_SCRATCH_BYTES of scratch */
 } dsa_status_t;
 
 typedef enum {
@@ -190,6 +195,32 @@ dsa_status_t dsa_forward_timed(const dsa_problem_t* prob,
                                hipEvent_t* events, int32_t n_events,
                                int32_t* n_chunks_out,
                                hipStream_t stream);
+
+/* dsa_forward for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ * Same arguments, results and launches as dsa_forward, but the workspace is
+ * a static device array inside the library, DSA_STATIC_SCRATCH_BYTES large,
+ * one per GPU: it is set up when the library's code is loaded on that GPU
+ * and held until the process ends; the first call on a device looks up its
+ * address there (hipGetSymbolAddress).  The call itself allocates nothing.
+ *   The problem's forward workspace (dsa_workspace_size(prob,
+ *   DSA_OP_FORWARD), less the top-k indices when topk_idx is given) must
+ *   fit: else DSA_ERR_EXCEEDS_SCRATCH, before any HIP call.  Both decode
+ *   shapes (32 x 32K and 8 x 128K) fit; long prefills do not.
+ *   Runs on the current device, which must be the stream's.  Every call on
+ *   one GPU works in that GPU's one array: calls whose stream work overlaps
+ *   on one GPU (other streams, other host threads) race and give undefined
+ *   results; calls in one stream's order are safe.  Nothing needs clearing
+ *   between calls (every byte read is written earlier in the same call).
+ */
+#define DSA_STATIC_SCRATCH_BYTES ((size_t)96 << 20)
+dsa_status_t dsa_forward_static(const dsa_problem_t* prob,
+                                const void* q_idx, const uint8_t* q_scale,
+                                const void* k_idx, const uint8_t* k_scale,
+                                const float* head_w,
+                                const void* q_attn, const void* kv,
+                                int32_t* topk_idx, void* out, float* lse,
+                                hipStream_t stream);
 
 /* Cache append (HF doc "DeepSeek-V3.2", section "DeepSeek Sparse Attention
  * (DSA)": the indexer keeps its own cache of single-head index keys next to

@@ -4,6 +4,7 @@
 #include "dsa.h"
 #include "dsa_internal.h"
 
+#include <atomic>
 #include <cmath>
 #include <cstdint>
 
@@ -358,6 +359,52 @@ dsa_status_t dsa_forward_timed(const dsa_problem_t* prob, const void* q_idx, con
                       workspace_bytes, sink, n_chunks_out, stream);
 }
 
+// ------------------------------------------------------ allocation-free ---
+namespace {
+
+// dsa_forward_static's workspace: one copy of this array per GPU, created
+// when the code object is loaded there and kept until the process ends.  In
+// host code the name only stands for the symbol; kernels get the device
+// address hipGetSymbolAddress gives for the current GPU.
+static __device__ __align__(256) unsigned char scratch[DSA_STATIC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch_addr[kMaxDevices];
+
+// Device address of the current GPU's scratch array, looked up on the first
+// call on that device (null if the device or the lookup fails).
+void* static_scratch() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  void* p = g_scratch_addr[dev].load(std::memory_order_acquire);
+  if (p) return p;
+  if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return nullptr;
+  g_scratch_addr[dev].store(p, std::memory_order_release);
+  return p;
+}
+
+}  // namespace
+
+dsa_status_t dsa_forward_static(const dsa_problem_t* prob, const void* q_idx, const uint8_t* q_scale,
+                                const void* k_idx, const uint8_t* k_scale, const float* head_w,
+                                const void* q_attn, const void* kv, int32_t* topk_idx, void* out, float* lse,
+                                hipStream_t stream) {
+  // every argument check before the first HIP call
+  Path path;
+  dsa_status_t st = check_problem(prob, &path);
+  if (st != DSA_OK) return st;
+  if ((st = check_index_ptrs(path, q_idx, q_scale, k_idx, k_scale, head_w)) != DSA_OK) return st;
+  if ((st = check_attn_ptrs(q_attn, kv, out)) != DSA_OK) return st;
+  if ((topk_idx && !aligned16(topk_idx)) || (lse && !aligned16(lse))) return DSA_ERR_INVALID_ARGUMENT;
+  if (plan_forward(*prob, path, topk_idx == nullptr).total() > DSA_STATIC_SCRATCH_BYTES)
+    return DSA_ERR_EXCEEDS_SCRATCH;
+  void* ws = static_scratch();
+  if (!ws) return DSA_ERR_HIP;
+  EventSink none{nullptr, 0, stream};
+  return forward_impl(prob, q_idx, q_scale, k_idx, k_scale, head_w, q_attn, kv, topk_idx, out, lse, ws,
+                      DSA_STATIC_SCRATCH_BYTES, none, nullptr, stream);
+}
+
 size_t dsa_workspace_size(const dsa_problem_t* prob, int32_t op) {
   Path path;
   if (check_problem(prob, &path) != DSA_OK) return 0;
@@ -478,6 +525,7 @@ const char* dsa_status_string(dsa_status_t s) {
     case DSA_ERR_UNSUPPORTED: return "unsupported problem (dtype combination or dims)";
     case DSA_ERR_WORKSPACE_TOO_SMALL: return "workspace too small";
     case DSA_ERR_HIP: return "HIP runtime or launch error";
+    case DSA_ERR_EXCEEDS_SCRATCH: return "problem needs more than the library's static scratch (DSA_STATIC_SCRATCH_BYTES)";
   }
   return "unknown status";
 }

@@ -17,7 +17,9 @@ import torch
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libdsa.so")
 
-DSA_OK, DSA_ERR_INVALID_ARGUMENT, DSA_ERR_UNSUPPORTED, DSA_ERR_WORKSPACE_TOO_SMALL, DSA_ERR_HIP = range(5)
+DSA_OK, DSA_ERR_INVALID_ARGUMENT, DSA_ERR_UNSUPPORTED, DSA_ERR_WORKSPACE_TOO_SMALL, DSA_ERR_HIP, \
+    DSA_ERR_EXCEEDS_SCRATCH = range(6)
+DSA_STATIC_SCRATCH_BYTES = 96 << 20
 DSA_F32, DSA_BF16, DSA_FP8_E4M3 = 0, 1, 2
 DSA_OP_ATTN, DSA_OP_FORWARD, DSA_OP_TOPK = 1, 2, 3
 DSA_NUM_STAGES = 4
@@ -64,6 +66,7 @@ def lib() -> ctypes.CDLL:
         "dsa_sparse_mla_attn": [P, V, V, V, V, V, V, SZ, V],
         "dsa_forward": [P, V, V, V, V, V, V, V, V, V, V, V, SZ, V],
         "dsa_forward_timed": [P, V, V, V, V, V, V, V, V, V, V, V, SZ, V, I32, V, V],
+        "dsa_forward_static": [P, V, V, V, V, V, V, V, V, V, V, V],
     }
     for name, args in sigs.items():
         f = getattr(L, name)
@@ -379,6 +382,20 @@ def forward(p: Problem, q_idx, q_scale, k_idx, k_scale, head_w, q_attn, kv, out=
         st = lib().dsa_forward_timed(ctypes.byref(p), *iargs, qa, kvp, ip, op, lp, wsp, ws.numel(),
                                      events, n_events, None, _stream())
     _check(st, "dsa_forward")
+    return out, lse, topk_idx
+
+
+def forward_static(p: Problem, q_idx, q_scale, k_idx, k_scale, head_w, q_attn, kv, out=None, lse=None,
+                   topk_idx=None):
+    """forward() working in the library's static per-GPU scratch instead of a
+    workspace (dsa_forward_static: no device allocation inside the call when
+    out is given).  Returns (out, lse, topk_idx)."""
+    if out is None:
+        out = _out_tensor(p, q_attn.device)
+    iargs = _index_args(p, q_idx, q_scale, k_idx, k_scale, head_w)
+    qa, kvp, op, lp = _attn_args(p, q_attn, kv, out, lse)
+    ip = _ptr(topk_idx, "topk_idx", torch.int32, (p.batch, p.q_len, p.topk), allow_none=True)
+    _check(lib().dsa_forward_static(ctypes.byref(p), *iargs, qa, kvp, ip, op, lp, _stream()), "dsa_forward_static")
     return out, lse, topk_idx
 
 

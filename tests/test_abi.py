@@ -37,11 +37,11 @@ def test_library_exports_every_declared_symbol(dsa):
     L = dsa.lib()
     for name in _declared_functions():
         assert hasattr(L, name), name
-    assert dsa.abi_version() == 4
+    assert dsa.abi_version() == 5
 
 
 def test_status_strings(dsa):
-    for s in range(5):
+    for s in range(6):
         assert dsa.status_string(s)
 
 
@@ -180,6 +180,30 @@ def test_sliced_topk_plan_is_host_only_and_bounded(dsa):
     assert dsa.topk_slice_len(dsa.make_problem(C.DECODE_32K)) == 0
     assert dsa.topk_slice_len(_prob(dsa, C.DECODE_128K, batch=1)) == 1024
     assert dsa.topk_slice_len(_prob(dsa, C.DECODE_128K, q_len=0)) == 0
+
+
+def test_static_forward_checks_before_any_hip_call(dsa):
+    # fake but aligned device pointers: every rejection comes before the
+    # scratch lookup or a launch, so this runs without a GPU
+    L = dsa.lib()
+    v = ctypes.c_void_p(256)
+    big = dsa.make_problem(C.PREFILL_8K)
+    assert dsa.workspace_size(big, dsa.DSA_OP_FORWARD) > dsa.DSA_STATIC_SCRATCH_BYTES
+    args = [v] * 10 + [None]          # q_idx .. lse, stream
+    assert L.dsa_forward_static(ctypes.byref(big), *args) == dsa.DSA_ERR_EXCEEDS_SCRATCH
+    # both decode workloads fit, with or without top-k indices out
+    for cfg in (C.DECODE_32K, C.DECODE_128K):
+        assert dsa.workspace_size(dsa.make_problem(cfg), dsa.DSA_OP_FORWARD) <= dsa.DSA_STATIC_SCRATCH_BYTES
+    p = dsa.make_problem(C.DECODE_32K)
+    bad = list(args)
+    bad[0] = None                      # no q_idx
+    assert L.dsa_forward_static(ctypes.byref(p), *bad) == dsa.DSA_ERR_INVALID_ARGUMENT
+    bad = list(args)
+    bad[9] = ctypes.c_void_p(260)      # misaligned lse
+    assert L.dsa_forward_static(ctypes.byref(p), *bad) == dsa.DSA_ERR_INVALID_ARGUMENT
+    assert L.dsa_forward_static(None, *args) == dsa.DSA_ERR_INVALID_ARGUMENT
+    assert "static scratch" in dsa.status_string(dsa.DSA_ERR_EXCEEDS_SCRATCH)
+    assert dsa.DSA_STATIC_SCRATCH_BYTES == 96 << 20
 
 
 def test_topk_ws_rejects_small_workspace_before_launch(dsa):
