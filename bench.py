@@ -329,6 +329,9 @@ def main():
                     help="decode workloads: each step appends one token per sequence to caches with room for "
                          "them and runs the fused path for one query at the grown context; the `steps` "
                          "steps end at the workload's context")
+    ap.add_argument("--kv-len", type=int, default=None,
+                    help="decode workloads: run the workload at this context instead (same batch, top-k and "
+                         "planted fraction; the workload name gets ctx<kv-len>), for context sweeps")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a 1 GiB elementwise copy (for calibrating rocprofv3 byte counters)")
     args = ap.parse_args()
@@ -345,6 +348,16 @@ def main():
     from dsa_workloads import BY_NAME, generate
 
     cfg = BY_NAME[args.config]
+    if args.kv_len is not None:
+        if cfg.q_len > 4 or args.kv_len < cfg.topk or "_ctx" not in cfg.name:
+            print("--kv-len applies to decode workloads, at a context of at least top-k", file=sys.stderr)
+            sys.exit(2)
+        from dsa_workloads import scaled
+        plants = cfg.plant_count
+        if cfg.planting == "fraction":            # keep the planted fraction of the context
+            plants = max(1, round(cfg.plant_count * args.kv_len / cfg.kv_len))
+        cfg = scaled(cfg, kv_len=args.kv_len, plant_count=plants,
+                     name=cfg.name[:cfg.name.index("_ctx")] + f"_ctx{args.kv_len}")
     dev = "cuda:0"
     torch.cuda.set_device(0)
     if args.decode_loop:
