@@ -531,8 +531,16 @@ __device__ __forceinline__ void coh_store(uint32_t* p, uint32_t v) {
   __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// 16-byte loads that bypass the non-coherent cache levels (sc1), as the
+// agent-scope atomic loads do, for data other work-groups of the launch
+// wrote; a buffer resource keeps reads past `bytes` at zero.
+constexpr int kSc1 = 16;
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t coh_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, 0x00020000);
+}
+
 struct CoopShared {
-  uint32_t h[kBins1];                            // first-level histogram, then the 1024-bin passes
+  uint32_t h[kBins1];      // the slice's histogram, then the row's, then the 1024-bin passes
   uint32_t gt[kMaxSl];
   uint32_t eq[kMaxSl];
   uint32_t ws[kW];
@@ -576,10 +584,21 @@ __global__ __launch_bounds__(kT) void tk_coop_kernel(TopkLaunch a) {
     if (v) atomicAdd(&head[tid + kT * j], v);
   }
   row_barrier(head + kBins1, (uint32_t)np);
-  // 2. threshold bin; this slice's candidates (keys in b1) and counts
+  // 2. threshold bin (the row histogram comes in through LDS: coalesced
+  // 16-byte loads, then 16 consecutive bins per thread); this slice's
+  // candidates (keys in b1) and counts
+  {
+    const __amdgpu_buffer_rsrc_t hr = coh_rsrc(head, kBins1 * 4);
+#pragma unroll
+    for (int j = 0; j < kBins1 / (4 * kT); ++j) {
+      const int c = tid + kT * j;
+      st16(&sh.h[4 * c], __builtin_amdgcn_raw_buffer_load_b128(hr, 16 * c, 0, kSc1));
+    }
+  }
+  __syncthreads();
   uint32_t cnt[16];
 #pragma unroll
-  for (int j = 0; j < 16; ++j) cnt[j] = coh_load(&head[kBins1 - 1 - 16 * tid - j]);
+  for (int j = 0; j < 16; ++j) cnt[j] = sh.h[kBins1 - 1 - 16 * tid - j];
   uint32_t above;
   const uint32_t b1 = find_bin<16>(cnt, (uint32_t)K, sh.ws, sh.res, &above);
   const uint32_t r1 = (uint32_t)K - above;
@@ -611,16 +630,25 @@ __global__ __launch_bounds__(kT) void tk_coop_kernel(TopkLaunch a) {
     coh_store(&info[2 * rs.s + 1], tot >> 16);
   }
   row_barrier(head + kBins1 + 1, (uint32_t)np);
-  // 3. every slice's counts and candidates (fixed shares, as tk_emit_kernel)
+  // 3. every slice's counts and candidates: tps threads per slice, thread j
+  // of a slice holding its candidates 4(j + tps u) .. +3 (16-byte loads,
+  // a slice's threads reading consecutive bytes)
   const int tps = np <= kT ? kT / np : 0;
-  const int my_sl = tps ? tid % np : 0;
-  const int my_j0 = tps ? tid / np : 0;
+  const int my_sl = tps ? tid / tps : 0;
+  const int my_j = tps ? tid - my_sl * tps : 0;
   const bool my_on = tps && tid < np * tps;
   uint32_t ck[kCandRegs];
+  static_assert(kCandRegs % 4 == 0, "candidates load in groups of four");
+  {
+    const __amdgpu_buffer_rsrc_t cr = coh_rsrc(cand_row, (uint32_t)np * (uint32_t)L * 4u);
 #pragma unroll
-  for (int u = 0; u < kCandRegs; ++u) {
-    const int jj = my_j0 + u * tps;
-    ck[u] = my_on && jj < L ? coh_load(&cand_row[(int64_t)my_sl * L + jj]) : 0u;
+    for (int u = 0; u < kCandRegs / 4; ++u) {
+      const int jj = 4 * (my_j + u * tps);
+      const u32x4 v = my_on && jj < L ? __builtin_amdgcn_raw_buffer_load_b128(cr, 4 * (my_sl * L + jj), 0, kSc1)
+                                      : u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) ck[4 * u + e] = v[e];
+    }
   }
   const uint32_t my_ce = my_on ? coh_load(&info[2 * my_sl + 1]) : 0u;
   uint32_t ce[2], g0[2];
@@ -632,7 +660,7 @@ __global__ __launch_bounds__(kT) void tk_coop_kernel(TopkLaunch a) {
   }
 #pragma unroll
   for (int u = 0; u < kCandRegs; ++u)
-    if ((uint32_t)(my_j0 + u * tps) >= my_ce) ck[u] = 0u;
+    if ((uint32_t)(4 * (my_j + (u / 4) * tps) + (u % 4)) >= my_ce) ck[u] = 0u;
   const bool spill = !tps || ce[0] > (uint32_t)(tps * kCandRegs) || ce[1] > (uint32_t)(tps * kCandRegs);
   const bool held = !__syncthreads_or(spill);
   // candidates that did not fit the fixed shares: every slice's buffer is
