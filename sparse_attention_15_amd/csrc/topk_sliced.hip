@@ -189,6 +189,14 @@ __global__ __launch_bounds__(kT) void tk_hist_kernel(TopkLaunch a) {
 // nb = PER * kT bins, thread t owning bins nb-1-PER*t down to nb-PER*(t+1):
 // returns the bin and, in *above, the number of elements in higher bins.
 // cnt[] holds this thread's counts, highest bin first.  Contains barriers.
+// LDS histograms that find_bin reads as runs of PER consecutive bins per
+// thread: a pad word after every run puts neighbouring lanes' runs in
+// different banks (unpadded, lanes 16 or 4 words apart share a few banks).
+template <int PER>
+__device__ __forceinline__ int padded(int bin) { return bin + bin / PER; }
+constexpr int kPad1 = kBins1 + kBins1 / 16;     // 4096 bins read 16 per thread
+constexpr int kPad2 = kBins2 + kBins2 / 4;      // 1024 bins read 4 per thread
+
 template <int PER>
 __device__ __forceinline__ uint32_t find_bin(const uint32_t (&cnt)[PER], uint32_t k, uint32_t* ws, uint32_t* res,
                                              uint32_t* above) {
@@ -289,7 +297,7 @@ __global__ __launch_bounds__(kT) void tk_classify_kernel(TopkLaunch a) {
 constexpr int kCandRegs = 16;        // candidates held per thread (4096 per work-group)
 
 struct EmitShared {
-  uint32_t h[kBins2];
+  uint32_t h[kPad2];               // the 1024-bin passes (padded runs of 4)
   uint32_t cstart[kMaxSl + 1];     // flattened start of each slice's candidates
   uint32_t gt[kMaxSl];             // candidates above T per slice
   uint32_t eq[kMaxSl];             // candidates equal to T per slice
@@ -410,15 +418,15 @@ __global__ __launch_bounds__(kT) void tk_emit_kernel(TopkLaunch a, int L) {
     const int shift = pass == 0 ? 10 : 0;
     const int pshift = pass == 0 ? 20 : 10;
 #pragma unroll
-    for (int j = 0; j < kBins2 / kT; ++j) sh.h[tid + kT * j] = 0u;
+    for (int b = tid; b < kPad2; b += kT) sh.h[b] = 0u;
     __syncthreads();
     for_each([&](uint32_t key, int) {
-      if ((key >> pshift) == prefix) atomicAdd(&sh.h[(key >> shift) & (kBins2 - 1)], 1u);
+      if ((key >> pshift) == prefix) atomicAdd(&sh.h[padded<4>((key >> shift) & (kBins2 - 1))], 1u);
     });
     __syncthreads();
     uint32_t cnt[4];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) cnt[j] = sh.h[kBins2 - 1 - 4 * tid - j];
+    for (int j = 0; j < 4; ++j) cnt[j] = sh.h[padded<4>(kBins2 - 1 - 4 * tid - j)];
     uint32_t above;
     const uint32_t bin = find_bin<4>(cnt, need, sh.ws, sh.res, &above);
     prefix = (prefix << 10) | bin;
@@ -540,7 +548,7 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t coh_rsrc(const void* base, uin
 }
 
 struct CoopShared {
-  uint32_t h[kBins1];      // the slice's histogram, then the row's, then the 1024-bin passes
+  uint32_t h[kPad1];       // the slice's histogram, then the row's (padded), then the 1024-bin passes
   uint32_t gt[kMaxSl];
   uint32_t eq[kMaxSl];
   uint32_t ws[kW];
@@ -592,13 +600,15 @@ __global__ __launch_bounds__(kT) void tk_coop_kernel(TopkLaunch a) {
 #pragma unroll
     for (int j = 0; j < kBins1 / (4 * kT); ++j) {
       const int c = tid + kT * j;
-      st16(&sh.h[4 * c], __builtin_amdgcn_raw_buffer_load_b128(hr, 16 * c, 0, kSc1));
+      const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(hr, 16 * c, 0, kSc1);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) sh.h[padded<16>(4 * c) + e] = v[e];   // bins 4c..4c+3 share a run
     }
   }
   __syncthreads();
   uint32_t cnt[16];
 #pragma unroll
-  for (int j = 0; j < 16; ++j) cnt[j] = sh.h[kBins1 - 1 - 16 * tid - j];
+  for (int j = 0; j < 16; ++j) cnt[j] = sh.h[padded<16>(kBins1 - 1 - 16 * tid - j)];
   uint32_t above;
   const uint32_t b1 = find_bin<16>(cnt, (uint32_t)K, sh.ws, sh.res, &above);
   const uint32_t r1 = (uint32_t)K - above;
@@ -683,15 +693,15 @@ __global__ __launch_bounds__(kT) void tk_coop_kernel(TopkLaunch a) {
     const int shift = pass == 0 ? 10 : 0;
     const int pshift = pass == 0 ? 20 : 10;
 #pragma unroll
-    for (int j = 0; j < kBins2 / kT; ++j) sh.h[tid + kT * j] = 0u;
+    for (int b = tid; b < kPad2; b += kT) sh.h[b] = 0u;
     __syncthreads();
     for_each([&](uint32_t key, int) {
-      if ((key >> pshift) == prefix) atomicAdd(&sh.h[(key >> shift) & (kBins2 - 1)], 1u);
+      if ((key >> pshift) == prefix) atomicAdd(&sh.h[padded<4>((key >> shift) & (kBins2 - 1))], 1u);
     });
     __syncthreads();
     uint32_t c4[4];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) c4[j] = sh.h[kBins2 - 1 - 4 * tid - j];
+    for (int j = 0; j < 4; ++j) c4[j] = sh.h[padded<4>(kBins2 - 1 - 4 * tid - j)];
     uint32_t ab;
     const uint32_t bin = find_bin<4>(c4, need, sh.ws, sh.res, &ab);
     prefix = (prefix << 10) | bin;
