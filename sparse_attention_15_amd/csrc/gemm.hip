@@ -210,16 +210,28 @@ __global__ __launch_bounds__(NW * 64) void gemm_skinny_kernel(GemmLaunch g) {
 }
 
 // Split-K partials summed in split order (so the result does not depend on
-// scheduling), one thread per output.
+// scheduling), one thread per output.  The partials are loaded 16 at a time
+// before any is added: a loop of adds that each wait for their own load ran
+// at one memory round trip per split.
 __global__ __launch_bounds__(256) void gemm_split_reduce_kernel(GemmLaunch g) {
+  constexpr int kLd = 16;
   const int64_t per_b = (int64_t)g.M * g.N;
   const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (idx >= per_b * g.batch) return;
   const int bz = (int)(idx / per_b);
   const int64_t mn = idx - bz * per_b;
   const int m = (int)(mn / g.N), n = (int)(mn - (int64_t)m * g.N);
+  const float* src = g.part + (int64_t)bz * per_b + mn;
+  const int64_t split_stride = (int64_t)g.batch * per_b;
   float v = 0.f;
-  for (int kz = 0; kz < g.ksplit; ++kz) v += g.part[((int64_t)kz * g.batch + bz) * per_b + mn];
+  for (int k0 = 0; k0 < g.ksplit; k0 += kLd) {
+    float t[kLd];
+#pragma unroll
+    for (int j = 0; j < kLd; ++j) t[j] = k0 + j < g.ksplit ? src[(k0 + j) * split_stride] : 0.f;
+#pragma unroll
+    for (int j = 0; j < kLd; ++j)
+      if (k0 + j < g.ksplit) v += t[j];
+  }
   void* cb = g.c_f32 ? (void*)(static_cast<float*>(g.C) + (int64_t)bz * g.sc)
                      : (void*)(static_cast<uint16_t*>(g.C) + (int64_t)bz * g.sc);
   store_c(g, cb, m, n, v);
