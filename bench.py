@@ -125,6 +125,28 @@ def kernel_units(cfg, kernel, al, n_chunks, split_rows):
             "bytes per launch: split partials (output precision) and LSEs read + out and lse written")
 
 
+DECODE_HBM_TARGET = 0.60        # decode-shaped path: fraction of HBM bandwidth
+PREFILL_INDEX_TARGET = 0.50     # prefill-shaped indexer: fraction of the bf16 MFMA peak
+
+
+def path_target(cfg, al, path_bytes, ms_per_step, index_ms):
+    """The step against the path-level targets: decode-shaped workloads move
+    the path's algorithmic bytes at >= 60% of HBM; prefill-shaped ones run
+    the indexer at >= 50% of the bf16 MFMA peak (index_ms: the indexer's
+    event time per step)."""
+    if cfg.q_len <= 4:
+        frac = path_bytes / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS
+        need_ms = path_bytes / (DECODE_HBM_TARGET * HBM_PEAK_GBS * 1e9) * 1e3
+        return {"what": "decode path algorithmic bytes at >= 60% of 8 TB/s", "value": round(frac, 4),
+                "goal": DECODE_HBM_TARGET, "met": frac >= DECODE_HBM_TARGET,
+                "goal_ms_per_step": round(need_ms, 5), "gap_ms_per_step": round(max(0.0, ms_per_step - need_ms), 5)}
+    if cfg.index_dtype == "f32":
+        return None
+    frac = al["index_flops"] / (index_ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS
+    return {"what": "prefill indexer flops at >= 50% of the 2.5 PFLOP/s bf16 peak (indexer event time)",
+            "value": round(frac, 4), "goal": PREFILL_INDEX_TARGET, "met": frac >= PREFILL_INDEX_TARGET}
+
+
 class _Same:
     """Indexable stand-in that returns one host array for any key."""
 
@@ -569,6 +591,7 @@ def main():
         "path_algorithmic_bytes": path_bytes,
         "path_mfma_frac_bf16": round((al["index_flops"] + al["attn_flops"]) / (ms_per_step * 1e-3) / 1e12
                                      / MFMA_BF16_PEAK_TFLOPS, 4),
+        "target": path_target(cfg, al, path_bytes, ms_per_step, stage_ms[0]),
     }
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(cfg, sets)
