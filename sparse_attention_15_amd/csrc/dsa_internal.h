@@ -56,8 +56,9 @@ struct AttnLaunch {
   const int32_t* idx;      // [B][Lq][K] (full-tensor numbering)
   void* out;               // [B][Lq][NH][Dv]
   float* lse;              // [B][Lq][NH] or null
-  void* part_o;            // split partials [rows][S][NH][Dv] (S > 1 only), in the
-                           // output's precision: fp32 for fp32 out, bf16 for bf16 out
+  void* part_o;            // split partials, NH x Dv values per (row, split) (S > 1 only),
+                           // in the output's precision (fp32 or bf16) and in the attention
+                           // kernel's register order (see its epilogue)
   float* part_lse;         // [rows][S][NH]
   int B, Lq, Lk, NH, Dqk, Dv, K;
   int Lc;                  // tokens per sequence in the latent cache (>= Lk)

@@ -502,21 +502,44 @@ __global__ __launch_bounds__(kWavesA * 64, 1) void attn_bf16_kernel(AttnLaunch a
   const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
   const float lse = l_tot > 0.f ? (st.m_run + log2f(l_tot)) * kLn2 : kNegInf;
 
-  // Output rows (out, or this split's partials) through LDS: per pass the
-  // wave writes a slice of its 32 head rows (512 bytes each) into the now
-  // idle stage buffers, then stores 1 KB contiguous per instruction (two
-  // 512-byte row segments) instead of 16 bytes into each of 32 rows.
-  __syncthreads();                                // every wave is done with the stage buffers
   const bool f32 = a.out_f32 != 0;
-  uint8_t* dst_base;
-  if (a.splits == 1) {
-    dst_base = static_cast<uint8_t*>(a.out) + (qrow * kNH + 32 * wave) * (int64_t)kDv * (f32 ? 4 : 2);
-    if (a.lse && hf == 0) a.lse[qrow * kNH + h] = lse;
-  } else {
+  if (a.splits > 1) {
+    // A split's partial leaves straight from the accumulators in their
+    // register order (no LDS round trip, no barrier): for value tile vt and
+    // quad q the wave stores its 64 lanes' four values contiguously, 512
+    // bytes (bf16) or 1 KB (fp32) per instruction.  Value r of lane l in
+    // block (wave w, vt, q) is O[head 32w + l % 32][dim 32vt + 8q + 4(l / 32) + r];
+    // attn_combine_kernel reads this layout.
     const int64_t prow = (int64_t)rr * a.splits + split;
-    dst_base = static_cast<uint8_t*>(a.part_o) + (prow * kNH + 32 * wave) * (int64_t)kDv * (f32 ? 4 : 2);
     if (hf == 0) a.part_lse[prow * kNH + h] = lse;
+    const int64_t blk0 = (prow * kWavesA + wave) * kVTiles * 4;   // this wave's first (vt, q) block
+    if (f32) {
+      f32x4* dst = static_cast<f32x4*>(a.part_o) + blk0 * 64 + lane;
+#pragma unroll
+      for (int vt = 0; vt < kVTiles; ++vt)
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          dst[(vt * 4 + q) * 64] = f32x4{st.o[vt][4 * q] * inv, st.o[vt][4 * q + 1] * inv,
+                                         st.o[vt][4 * q + 2] * inv, st.o[vt][4 * q + 3] * inv};
+    } else {
+      u32x2* dst = static_cast<u32x2*>(a.part_o) + blk0 * 64 + lane;
+#pragma unroll
+      for (int vt = 0; vt < kVTiles; ++vt)
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          dst[(vt * 4 + q) * 64] = u32x2{pack_bf16x2(st.o[vt][4 * q] * inv, st.o[vt][4 * q + 1] * inv),
+                                         pack_bf16x2(st.o[vt][4 * q + 2] * inv, st.o[vt][4 * q + 3] * inv)};
+    }
+    return;
   }
+
+  // Output rows through LDS: per pass the wave writes a slice of its 32 head
+  // rows (512 bytes each) into the now idle stage buffers, then stores 1 KB
+  // contiguous per instruction (two 512-byte row segments) instead of 16
+  // bytes into each of 32 rows.
+  __syncthreads();                                // every wave is done with the stage buffers
+  uint8_t* dst_base = static_cast<uint8_t*>(a.out) + (qrow * kNH + 32 * wave) * (int64_t)kDv * (f32 ? 4 : 2);
+  if (a.lse && hf == 0) a.lse[qrow * kNH + h] = lse;
   constexpr int kEpiRow = 528;                    // 512 bytes + 16 bytes of padding per head row
   uint8_t* ebuf = stg + wave * 32 * kEpiRow;
   const int row_bytes = kDv * (f32 ? 4 : 2);
@@ -559,73 +582,119 @@ __global__ __launch_bounds__(kWavesA * 64, 1) void attn_bf16_kernel(AttnLaunch a
 }
 
 // Merge split partials: out = sum_s exp(lse_s - LSE) * O_s, LSE = log sum_s exp(lse_s).
-// grid (NH / 4, rows), 256 threads: 64 per head, 8 value dims (one 16-byte
-// bf16 load, or two fp32 ones, per split) per thread; partials in the
-// output's precision.  S (the split count, a power of two) is a template
-// parameter so that all of a thread's loads are in flight together.
+// The partials are in the attention kernel's register order (see its
+// epilogue).  grid (32, rows): work-group x covers heads 32w .. 32w+31
+// (w = x / 8) and value tiles 2vg, 2vg+1, i.e. dims 64vg .. 64vg+63
+// (vg = x % 8): a 4 KB (bf16) or 8 KB (fp32) block of each split's
+// partial.  Thread t takes that block's 16-byte-aligned pair of lanes
+// 2t, 2t+1 (two heads, four dims each), loads it for G splits at a time
+// (all in flight together), adds the splits in order with fp32 weights and
+// stores its two 4-dim pieces.  The 32 heads' weights come from their LSEs
+// while the partials load.
+constexpr int kCombVT = 2;                        // value tiles per combine work-group
 template <int S, bool F32>
 __global__ __launch_bounds__(256) void attn_combine_kernel(AttnLaunch a) {
-  int hx = blockIdx.x, rr = blockIdx.y;
-  if ((gridDim.y & 7) == 0) {                   // row rr on the XCD its splits ran on
+  constexpr int EB = F32 ? 4 : 2;                 // bytes per value
+  constexpr int LD = 2 * 4 * EB / 16;             // 16-byte loads per thread and split
+  constexpr int G = (F32 ? 8 : 16) < S ? (F32 ? 8 : 16) : S;   // splits in flight at once
+  constexpr int NVG = kVTiles / kCombVT;          // work-groups per 32 heads
+  __shared__ float wt[S][32];
+  int gx = blockIdx.x, rr = blockIdx.y;
+  if ((gridDim.y & 7) == 0) {                     // row rr on the XCD its splits ran on
     const int lin = blockIdx.x + gridDim.x * blockIdx.y;
     const int loc = lin >> 3;
     rr = (lin & 7) + 8 * (loc / gridDim.x);
-    hx = loc - (loc / gridDim.x) * gridDim.x;
+    gx = loc - (loc / gridDim.x) * gridDim.x;
   }
-  const int h = 4 * hx + (threadIdx.x >> 6), v = 8 * (threadIdx.x & 63);
-  const int NH = a.NH, Dv = a.Dv;
+  const int w = gx / NVG, vg = gx - w * NVG, tid = threadIdx.x;
+  const int NH = a.NH;
   const int b = rr / a.q_count;
   const int i = a.q_begin + rr % a.q_count;
   const int64_t qrow = (int64_t)b * a.Lq + i;
-  const float* pl = a.part_lse + (int64_t)rr * S * NH + h;
-  float ls[S];
-  f32x4 pf[F32 ? S : 1][2];                       // fp32 partials
-  u32x4 pb[F32 ? 1 : S];                          // bf16 partials
+  // this thread's lanes l0, l0+1 of block (w, vt, q) of every split
+  const int c = 2 * tid;                          // chunk within the 512 chunks of (w, vg)
+  const int vt = kCombVT * vg + (c >> 8), q = (c >> 6) & 3, l0 = c & 63;
+  const int64_t split_u4 = (int64_t)NH * a.Dv * EB / 16;          // 16-byte units per split
+  const u32x4* src = static_cast<const u32x4*>(a.part_o) + (int64_t)rr * S * split_u4 +
+                     ((((int64_t)w * kVTiles + vt) * 4 + q) * 64 + l0) * (4 * EB) / 16;
+  u32x4 v[G][LD];
 #pragma unroll
-  for (int s = 0; s < S; ++s) {
-    ls[s] = pl[(int64_t)s * NH];
-    const int64_t off = (((int64_t)rr * S + s) * NH + h) * Dv + v;
-    if constexpr (F32) {
-      const f32x4* q = reinterpret_cast<const f32x4*>(static_cast<const float*>(a.part_o) + off);
-      pf[s][0] = q[0];
-      pf[s][1] = q[1];
-    } else {
-      pb[s] = ld16(static_cast<const uint16_t*>(a.part_o) + off);
-    }
-  }
-  float m = kNegInf;
+  for (int s = 0; s < G; ++s)
 #pragma unroll
-  for (int s = 0; s < S; ++s) m = fmaxf(m, ls[s]);
-  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-  float sum = 0.f;
-  if (m != kNegInf) {
+    for (int k = 0; k < LD; ++k) v[s][k] = src[s * split_u4 + k];
+  if (tid < 32) {
+    const int h = 32 * w + tid;
+    const float* pl = a.part_lse + (int64_t)rr * S * NH + h;
+    float m = kNegInf;
+#pragma unroll
+    for (int s = 0; s < S; ++s) m = fmaxf(m, pl[(int64_t)s * NH]);
+    float sum = 0.f;
 #pragma unroll
     for (int s = 0; s < S; ++s) {
-      if (ls[s] == kNegInf) continue;             // an empty split holds zeros
-      const float wgt = __expf(ls[s] - m);
-      sum += wgt;
+      const float ls = pl[(int64_t)s * NH];
+      const float e = (m == kNegInf || ls == kNegInf) ? 0.f : __expf(ls - m);   // an empty split holds zeros
+      wt[s][tid] = e;
+      sum += e;
+    }
+    const float inv = sum > 0.f ? 1.f / sum : 0.f;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        float x;
-        if constexpr (F32) x = pf[s][e >> 2][e & 3];
-        else x = (e & 1) ? bf16_hi(pb[s][e >> 1]) : bf16_lo(pb[s][e >> 1]);
-        acc[e] += wgt * x;
+    for (int s = 0; s < S; ++s) wt[s][tid] *= inv;
+    if (a.lse && vg == 0) a.lse[qrow * NH + h] = m == kNegInf ? kNegInf : m + __logf(sum);
+  }
+  __syncthreads();
+  const int hl = l0 & 31, hf = l0 >> 5;           // heads hl, hl+1; dims 32vt + 8q + 4hf + r
+  float acc[2][4];
+#pragma unroll
+  for (int j = 0; j < 2; ++j)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) acc[j][r] = 0.f;
+  auto add = [&](int s0) {
+#pragma unroll
+    for (int s = 0; s < G; ++s) {
+      float x[8];                                 // lane l0 + j, value r at 4j + r
+      if constexpr (F32) {
+#pragma unroll
+        for (int k = 0; k < LD; ++k) {
+          const f32x4 f = __builtin_bit_cast(f32x4, v[s][k]);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) x[4 * k + e] = f[e];
+        }
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          x[2 * e] = bf16_lo(v[s][0][e]);
+          x[2 * e + 1] = bf16_hi(v[s][0][e]);
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const float wj = wt[s0 + s][hl + j];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) acc[j][r] += wj * x[4 * j + r];
       }
     }
-    const float inv = 1.f / sum;
+  };
+  add(0);
 #pragma unroll
-    for (int e = 0; e < 8; ++e) acc[e] *= inv;
+  for (int s0 = G; s0 < S; s0 += G) {
+#pragma unroll
+    for (int s = 0; s < G; ++s)
+#pragma unroll
+      for (int k = 0; k < LD; ++k) v[s][k] = src[(s0 + s) * split_u4 + k];
+    add(s0);
   }
-  if constexpr (F32) {
-    float* o = static_cast<float*>(a.out) + (qrow * NH + h) * Dv + v;
-    *reinterpret_cast<f32x4*>(o) = f32x4{acc[0], acc[1], acc[2], acc[3]};
-    *reinterpret_cast<f32x4*>(o + 4) = f32x4{acc[4], acc[5], acc[6], acc[7]};
-  } else {
-    st16(static_cast<uint16_t*>(a.out) + (qrow * NH + h) * Dv + v,
-         u32x4{pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3]), pack_bf16x2(acc[4], acc[5]),
-               pack_bf16x2(acc[6], acc[7])});
+  // out[head 32w + hl + j][dims 32vt + 8q + 4hf .. +3]: per store
+  // instruction the wave's 64 pieces land as 64-byte runs of 16 head rows
+  const int d0 = 32 * vt + 8 * q + 4 * hf;
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    uint8_t* o = static_cast<uint8_t*>(a.out) + ((qrow * NH + 32 * w + hl + j) * (int64_t)a.Dv + d0) * EB;
+    if constexpr (F32) {
+      *reinterpret_cast<f32x4*>(o) = f32x4{acc[j][0], acc[j][1], acc[j][2], acc[j][3]};
+    } else {
+      *reinterpret_cast<u32x2*>(o) = u32x2{pack_bf16x2(acc[j][0], acc[j][1]), pack_bf16x2(acc[j][2], acc[j][3])};
+    }
   }
-  if (a.lse && (threadIdx.x & 63) == 0) a.lse[qrow * NH + h] = m == kNegInf ? kNegInf : m + __logf(sum);
 }
 
 // ------------------------------------------------------------- fp32 -------
@@ -716,7 +785,7 @@ hipError_t launch_attn_bf16(const AttnLaunch& a, hipStream_t s) {
 
 template <bool F32>
 hipError_t launch_combine_t(const AttnLaunch& a, hipStream_t s) {
-  dim3 grid(a.NH / 4, a.B * a.q_count);
+  dim3 grid(4 * (kVTiles / kCombVT), a.B * a.q_count);
   dim3 block(256);
   switch (a.splits) {
     case 2: hipLaunchKernelGGL((attn_combine_kernel<2, F32>), grid, block, 0, s, a); break;
@@ -729,9 +798,9 @@ hipError_t launch_combine_t(const AttnLaunch& a, hipStream_t s) {
   return hipGetLastError();
 }
 
-// bf16 kernel shapes only: NH = 128, Dv = 512 (64 threads x 8 dims per head)
+// bf16 kernel shapes only: NH = 128, Dv = 512 (the attention kernel's register order)
 hipError_t launch_attn_combine(const AttnLaunch& a, hipStream_t s) {
-  if (a.NH % 4 != 0 || a.Dv != 512) return hipErrorInvalidValue;
+  if (a.NH != kNH || a.Dv != kDv) return hipErrorInvalidValue;
   return a.out_f32 ? launch_combine_t<true>(a, s) : launch_combine_t<false>(a, s);
 }
 
