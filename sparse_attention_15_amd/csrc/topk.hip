@@ -523,9 +523,14 @@ void launch_rows(const TopkLaunch& a, int n_max, int grid, hipStream_t s) {
   const int chunks = (n_max + 3) / 4;
   const int iters = (chunks + kThreads - 1) / kThreads;
   // short rows come in large numbers (prefill): small histograms keep two
-  // work-groups per CU; long rows are few and get the widest spreading
+  // work-groups per CU; long rows are few and get the widest spreading.
+  // Many rows of up to 32768 positions (long prefills) take 4 copies, which
+  // fit two work-groups per CU (64K FP8 prefill: top-k 4.30 -> 3.96 ms per
+  // step); a decode batch of such rows keeps 8.
   if (iters <= 2)
     hipLaunchKernelGGL((topk_kernel<2, 2>), dim3(grid), dim3(kThreads), 0, s, a);
+  else if (iters <= 8 && grid >= 512)
+    hipLaunchKernelGGL((topk_kernel<8, 4>), dim3(grid), dim3(kThreads), 0, s, a);
   else if (iters <= 8)
     hipLaunchKernelGGL((topk_kernel<8, 8>), dim3(grid), dim3(kThreads), 0, s, a);
   else if (iters <= 16)
