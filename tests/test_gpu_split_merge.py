@@ -40,7 +40,8 @@ def _case(big_batch, lk, k, seed):
     return cfg, inp, idx.view(big_batch, 1, k).to(torch.int32).to(DEV)
 
 
-@pytest.mark.parametrize("lk,k", [(4096, 2048), (9000, 2048), (3000, 300)])
+# two rows split 16 (2048 keys), 4 (512) or 2 (300) ways
+@pytest.mark.parametrize("lk,k", [(4096, 2048), (9000, 2048), (3000, 512), (3000, 300)])
 def test_split_merge_against_unsplit(lk, k):
     """Split and unsplit launches round the bf16 probabilities of the PV
     product against different running maxima, so they agree to that
@@ -66,7 +67,8 @@ def test_split_merge_against_unsplit(lk, k):
     np.testing.assert_allclose(lse_s.cpu().numpy(), lse_b[:2].cpu().numpy(), rtol=1e-5, atol=1e-5)
 
 
-@pytest.mark.parametrize("lk,k", [(4096, 2048), (20000, 2048), (3000, 300)])
+# two rows split 16, 32 (4096 keys), 4 or 2 ways
+@pytest.mark.parametrize("lk,k", [(4096, 2048), (20000, 2048), (9000, 4096), (3000, 512), (3000, 300)])
 def test_split_merge_bf16_output_within_double_rounding_of_fp32(lk, k):
     """Same launch plan, two output types.  The fp32 output merges fp32
     partials; the bf16 one merges bf16-rounded partials O_s (each off by at
