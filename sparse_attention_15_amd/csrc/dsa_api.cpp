@@ -15,7 +15,10 @@ namespace {
 constexpr size_t kAlign = 256;
 constexpr size_t kScoresBudget = size_t(256) << 20;   // bytes of scores per query chunk
 constexpr int64_t kMaxLk = int64_t(1) << 24;
-constexpr int64_t kMaxLkBf16 = int64_t(1) << 21;       // row gathers use 32-bit byte offsets (1152 B rows)
+// Row gathers address a sequence's latent rows with byte offsets below 2^31
+// (1152-byte rows).
+constexpr int64_t kMaxLkBf16 = DSA_MAX_KV_LEN_BF16;
+static_assert(kMaxLkBf16 * 1152 <= (int64_t(1) << 31) - 1, "gather offsets stay below 2^31");
 
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }

@@ -112,7 +112,10 @@ def test_invalid_arguments_are_rejected_before_launch(dsa):
     # unsupported: bf16 with non-V3.2 dims, mixed f32/bf16
     assert _call_forward(dsa, _prob(dsa, C.DECODE_32K, index_heads=32)) == dsa.DSA_ERR_UNSUPPORTED
     assert _call_forward(dsa, _prob(dsa, C.DECODE_32K, index_dtype=dsa.DSA_F32)) == dsa.DSA_ERR_UNSUPPORTED
-    assert _call_forward(dsa, _prob(dsa, C.DECODE_32K, kv_len=(1 << 21) + 1)) == dsa.DSA_ERR_UNSUPPORTED
+    # latent gathers keep byte offsets below 2^31: (2^31 - 1) // 1152 rows
+    assert (2 ** 31 - 1) // 1152 == 1864135
+    assert _call_forward(dsa, _prob(dsa, C.DECODE_32K, kv_len=1864135 + 1)) == dsa.DSA_ERR_UNSUPPORTED
+    assert dsa.workspace_size(_prob(dsa, C.DECODE_32K, batch=1, kv_len=1864135), dsa.DSA_OP_FORWARD) > 0
     assert _call_forward(dsa, _prob(dsa, C.DECODE_32K, topk=65537)) == dsa.DSA_ERR_UNSUPPORTED
     # fp8 without scales
     p8 = dsa.make_problem(C.PREFILL_64K_FP8)
@@ -167,7 +170,7 @@ def test_sliced_topk_plan_is_host_only_and_bounded(dsa):
     assert dsa.workspace_size(dsa.make_problem(C.PREFILL_8K), dsa.DSA_OP_TOPK) == 0
     assert dsa.workspace_size(_prob(dsa, C.DECODE_128K, batch=200), dsa.DSA_OP_TOPK) == 0
     assert dsa.workspace_size(_prob(dsa, C.DECODE_128K, kv_len=65535), dsa.DSA_OP_TOPK) == 0
-    for batch, lk, k in ((1, 65536, 1), (8, 131072, 2048), (1, 1 << 21, 2048), (128, 70000, 4999), (3, 70001, 7)):
+    for batch, lk, k in ((1, 65536, 1), (8, 131072, 2048), (1, 1864135, 2048), (128, 70000, 4999), (3, 70001, 7)):
         n = dsa.workspace_size(_prob(dsa, C.DECODE_128K, batch=batch, kv_len=lk, topk=k), dsa.DSA_OP_TOPK)
         # row head + per-slice counts + row info + a (key, position) pair and a key per position
         assert n >= batch * ((4096 + 64) * 4 + 512 * 8 + 16 + lk * 12), (batch, lk, k)

@@ -377,7 +377,14 @@ def _sample_rows(cfg, k):
     return rows
 
 
-@pytest.mark.parametrize("cfg", [C.DECODE_32K, C.PREFILL_8K, C.DECODE_128K, C.PREFILL_64K_FP8], ids=lambda c: c.name)
+# The longest context the bf16 path accepts: one decode row whose latent
+# gathers reach byte offsets just below 2^31 (1864135 rows of 1152 bytes);
+# 456 top-k slices of 4096 positions.
+MAX_CONTEXT = C.scaled(C.DECODE_128K, name="decode_bf16_B1_ctx1864135", batch=1, kv_len=1864135)
+
+
+@pytest.mark.parametrize("cfg", [C.DECODE_32K, C.PREFILL_8K, C.DECODE_128K, C.PREFILL_64K_FP8, MAX_CONTEXT],
+                         ids=lambda c: c.name)
 def test_full_size_sampled_rows(cfg):
     """Full-size workloads, same launch configuration as the bench, sampled rows vs the oracle."""
     inp = generate(cfg, device=DEV)
