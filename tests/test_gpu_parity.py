@@ -365,6 +365,50 @@ def test_forward_wide_cases(case):
     _check_forward(cfg, inp, host, out, idx, lse, rows=rows, label=name)
 
 
+@pytest.mark.parametrize("shape", [
+    dict(base="decode", batch=2, q_len=1, kv_len=9000, topk=2048, out="bf16"),   # 16 splits
+    dict(base="decode", batch=2, q_len=1, kv_len=9000, topk=2048, out="f32"),
+    dict(base="decode", batch=3, q_len=2, kv_len=900, topk=300, out="bf16"),     # 2 splits
+    dict(base="tiny", batch=1, q_len=3, kv_len=40, topk=16, out="f32"),           # fp32 path
+], ids=["split16_bf16", "split16_f32", "split2_bf16", "f32_path"])
+def test_sparse_attention_empty_rows_and_splits(shape):
+    """A list with no usable entry gives out = 0 and lse = -inf; a list whose
+    usable entries all fall in its last split (the earlier splits empty)
+    matches the oracle on those entries."""
+    dsa = _dsa()
+    shape = dict(shape)
+    base = C.TINY if shape.pop("base") == "tiny" else C.DECODE_32K
+    od = shape.pop("out")
+    cfg = C.scaled(base, name="empty_rows", plant_count=0, **shape)
+    inp, host = _inputs(cfg)
+    B, Lq, K, Lk = cfg.batch, cfg.q_len, cfg.topk, cfg.kv_len
+    rng = np.random.default_rng(11)
+    idx = np.full((B, Lq, K), -1, dtype=np.int64)
+    for b in range(B):
+        for i in range(Lq):
+            n = Lk - Lq + i + 1
+            take = min(K, n)
+            idx[b, i, :take] = np.sort(rng.choice(n, size=take, replace=False))
+    idx[0, 0, :] = -1                               # no usable entry
+    keep = max(1, K // 8)                           # only the last entries usable
+    idx[B - 1, Lq - 1, :K - keep] = -1
+    p = dsa.make_problem(cfg, out_dtype=od)
+    lse = torch.empty(B, Lq, cfg.attn_heads, dtype=torch.float32, device=DEV)
+    out, lse = dsa.sparse_mla_attn(p, inp["q_attn"], inp["kv"], torch.from_numpy(idx.astype(np.int32)).to(DEV),
+                                   lse=lse)
+    torch.cuda.synchronize()
+    o, l = np64(out), lse.cpu().numpy()
+    assert np.all(o[0, 0] == 0.0) and np.all(np.isneginf(l[0, 0]))
+    tol = tol_for(cfg)
+    for b in range(B):
+        for i in range(Lq):
+            if (b, i) == (0, 0):
+                continue
+            ref_o, ref_l = O.sparse_attention_row(host["q_attn"][b, i], host["kv"][b], idx[b, i], cfg.softmax_scale,
+                                                  cfg.v_dim)
+            assert np.abs(o[b, i] - ref_o).max() <= tol and np.abs(l[b, i] - ref_l).max() <= tol, (b, i)
+
+
 # ------------------------------------------------------------ full size ----
 def _sample_rows(cfg, k):
     rows = []
