@@ -52,6 +52,11 @@ constexpr int kStageBytes = kBK * kLdsRow;      // one 32-row block in LDS
 constexpr int kDmaInstr = kBK * kLdsChunks / 64;  // 38 gather instructions per block
 constexpr int kMaxPer = 2048;                   // list entries per work-group
 constexpr float kTau = 8.0f;                    // lazy max threshold (log2 units)
+// Decode split partials in fp32 for bf16 outputs too (one output rounding
+// instead of two).  Off: it doubles the partial bytes, +8.4 us per 32 x 32K
+// decode step (attention +3.7, combine +4.3) and +2.7 us at 8 x 128K, while
+// the second rounding stays far inside the bf16 output tolerance.
+constexpr bool kF32Partials = false;
 
 #define LDS_PTR(p) ((__attribute__((address_space(3))) void*)(p))
 #define GLB_PTR(p) ((const __attribute__((address_space(1))) void*)(p))
@@ -504,6 +509,7 @@ __global__ __launch_bounds__(kWavesA * 64, 1) void attn_bf16_kernel(AttnLaunch a
 
   const bool f32 = a.out_f32 != 0;
   if (a.splits > 1) {
+    const bool pf32 = kF32Partials || f32;
     // A split's partial leaves straight from the accumulators in their
     // register order (no LDS round trip, no barrier): for value tile vt and
     // quad q the wave stores its 64 lanes' four values contiguously, 512
@@ -513,7 +519,7 @@ __global__ __launch_bounds__(kWavesA * 64, 1) void attn_bf16_kernel(AttnLaunch a
     const int64_t prow = (int64_t)rr * a.splits + split;
     if (hf == 0) a.part_lse[prow * kNH + h] = lse;
     const int64_t blk0 = (prow * kWavesA + wave) * kVTiles * 4;   // this wave's first (vt, q) block
-    if (f32) {
+    if (pf32) {
       f32x4* dst = static_cast<f32x4*>(a.part_o) + blk0 * 64 + lane;
 #pragma unroll
       for (int vt = 0; vt < kVTiles; ++vt)
@@ -594,9 +600,11 @@ __global__ __launch_bounds__(kWavesA * 64, 1) void attn_bf16_kernel(AttnLaunch a
 constexpr int kCombVT = 2;                        // value tiles per combine work-group
 template <int S, bool F32>
 __global__ __launch_bounds__(256) void attn_combine_kernel(AttnLaunch a) {
-  constexpr int EB = F32 ? 4 : 2;                 // bytes per value
+  constexpr bool PF32 = kF32Partials || F32;      // partial precision
+  constexpr int EB = PF32 ? 4 : 2;                // bytes per partial value
+  constexpr int OB = F32 ? 4 : 2;                 // bytes per output value
   constexpr int LD = 2 * 4 * EB / 16;             // 16-byte loads per thread and split
-  constexpr int G = (F32 ? 8 : 16) < S ? (F32 ? 8 : 16) : S;   // splits in flight at once
+  constexpr int G = (PF32 ? 8 : 16) < S ? (PF32 ? 8 : 16) : S;   // splits in flight at once
   constexpr int NVG = kVTiles / kCombVT;          // work-groups per 32 heads
   __shared__ float wt[S][32];
   int gx = blockIdx.x, rr = blockIdx.y;
@@ -652,7 +660,7 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnLaunch a) {
 #pragma unroll
     for (int s = 0; s < G; ++s) {
       float x[8];                                 // lane l0 + j, value r at 4j + r
-      if constexpr (F32) {
+      if constexpr (PF32) {
 #pragma unroll
         for (int k = 0; k < LD; ++k) {
           const f32x4 f = __builtin_bit_cast(f32x4, v[s][k]);
@@ -688,7 +696,7 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnLaunch a) {
   const int d0 = 32 * vt + 8 * q + 4 * hf;
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
-    uint8_t* o = static_cast<uint8_t*>(a.out) + ((qrow * NH + 32 * w + hl + j) * (int64_t)a.Dv + d0) * EB;
+    uint8_t* o = static_cast<uint8_t*>(a.out) + ((qrow * NH + 32 * w + hl + j) * (int64_t)a.Dv + d0) * OB;
     if constexpr (F32) {
       *reinterpret_cast<f32x4*>(o) = f32x4{acc[j][0], acc[j][1], acc[j][2], acc[j][3]};
     } else {
