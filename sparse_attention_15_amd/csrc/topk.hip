@@ -192,6 +192,24 @@ __global__ __launch_bounds__(kThreads, NC == 2 ? 8 : 4) void topk_kernel(TopkLau
     }
   };
 
+  // Pass 1 histograms (C copies) and pass 3's small one start at zero.
+  const uint32_t copy_base = (uint32_t)(lane & (C - 1)) * S;
+  const uint32_t pad = (uint32_t)(iters * kThreads * 4 - n);
+  auto clear_hists = [&]() {
+    for (int j = tid; j < C * kBins / 4; j += kThreads) {
+      const int r = j / (kBins / 4), o = j - r * (kBins / 4);
+      st16(&sh.hist[r * S + 4 * o], u32x4{0u, 0u, 0u, 0u});
+    }
+    if (tid < 64) st16(&sh.h3[4 * tid], u32x4{0u, 0u, 0u, 0u});
+    __syncthreads();
+    if (tid == 0 && pad != 0u) atomicSub(&sh.hist[0], pad);
+  };
+  auto count1 = [&](const uint32_t (&kk)[4]) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) atomicAdd(&sh.hist[copy_base + (kk[e] >> 20)], 1u);
+  };
+  bool counted = false;                           // pass 1 already counted while loading
+
   uint32_t keys[NC > 0 ? NC : 1][4];
   if constexpr (NC > 0) {
     // Every load of the row is issued before any is converted, so the
@@ -207,15 +225,13 @@ __global__ __launch_bounds__(kThreads, NC == 2 ? 8 : 4) void topk_kernel(TopkLau
     if (a.vec_ok && NC >= 8) {
       float vr[4] = {0.f, 0.f, 0.f, 0.f};        // the ragged chunk
       const int rpos = (crag * kThreads + tid) * 4;
-      if (crag < NC) {                            // lanes wholly inside still take one load
-        if (rpos + 3 < n) {
-          const f32x4 t = *reinterpret_cast<const f32x4*>(src + rpos);
+      if (crag < NC) {
+        // four clamped dword loads per lane, no lane-dependent branch (a
+        // branch around a load makes the other path wait for it before it
+        // writes the same registers, which serialised this load with the
+        // rest); positions past n read the last score and are masked below
 #pragma unroll
-          for (int e = 0; e < 4; ++e) vr[e] = t[e];
-        } else {
-#pragma unroll
-          for (int e = 0; e < 4; ++e) vr[e] = rpos + e < n ? src[rpos + e] : 0.f;
-        }
+        for (int e = 0; e < 4; ++e) vr[e] = src[min(rpos + e, n - 1)];
       }
       float v[NC][4];
 #pragma unroll
@@ -226,11 +242,18 @@ __global__ __launch_bounds__(kThreads, NC == 2 ? 8 : 4) void topk_kernel(TopkLau
         v[c][2] = t.z;
         v[c][3] = t.w;
       }
+      // The histograms are cleared while the loads are in flight; each
+      // chunk is then counted as soon as it has arrived (its conversion
+      // waits for that chunk only), so pass 1 overlaps the row's transfer.
+      clear_hists();
 #pragma unroll
-      for (int c = 0; c < NC; ++c)
+      for (int c = 0; c < NC; ++c) {
 #pragma unroll
         for (int e = 0; e < 4; ++e)
           keys[c][e] = inside(c, e) ? order_key(c < cfull ? v[c][e] : vr[e]) : 0u;
+        if (c < iters) count1(keys[c]);
+      }
+      counted = true;
     } else {
       // unaligned rows and short rows (one or two chunks: nothing to
       // overlap, and masked extra loads cost more than they hide): chunk by
@@ -256,20 +279,8 @@ __global__ __launch_bounds__(kThreads, NC == 2 ? 8 : 4) void topk_kernel(TopkLau
   //    cleared at the start, so no pass has a clearing step of its own.
   uint32_t prefix = 0, mask = 0, k_rem = (uint32_t)K;
   bool whole = false;                             // the last bin is taken whole
-  const uint32_t copy_base = (uint32_t)(lane & (C - 1)) * S;
-  const uint32_t pad = (uint32_t)(iters * kThreads * 4 - n);
-  for (int j = tid; j < C * kBins / 4; j += kThreads) {
-    const int r = j / (kBins / 4), o = j - r * (kBins / 4);
-    st16(&sh.hist[r * S + 4 * o], u32x4{0u, 0u, 0u, 0u});
-  }
-  if (tid < 64) st16(&sh.h3[4 * tid], u32x4{0u, 0u, 0u, 0u});
-  __syncthreads();
-  {
-    auto count1 = [&](const uint32_t (&kk)[4]) {
-#pragma unroll
-      for (int e = 0; e < 4; ++e) atomicAdd(&sh.hist[copy_base + (kk[e] >> 20)], 1u);
-    };
-    if (tid == 0 && pad != 0u) atomicSub(&sh.hist[0], pad);
+  if (!counted) {
+    clear_hists();
     if constexpr (NC > 0) {
 #pragma unroll
       for (int c = 0; c < NC; ++c)
@@ -281,6 +292,8 @@ __global__ __launch_bounds__(kThreads, NC == 2 ? 8 : 4) void topk_kernel(TopkLau
         count1(kk);
       }
     }
+  }
+  {
     __syncthreads();
     find_bin<C, true>(sh, sh.hist, kBins, k_rem);
     const uint32_t cnt = sh.cnt;
