@@ -94,7 +94,7 @@ ForwardPlan plan_forward(const dsa_problem_t& p, Path path, bool need_idx) {
   f.part_bytes = attn_partials_bytes(p, rows, attn_splits(p, path, rows));
   // few decode-shaped rows (the decode indexer kernel zeroes the histogram
   // the sliced selection accumulates into): one work-group per row slice
-  f.tk_sl_len = (path != kPathF32 && f.chunk <= 4) ? topk_sliced_len(rows, p.kv_len, p.topk) : 0;
+  f.tk_sl_len = (path != kPathF32 && f.chunk <= kDecodeIndexQueries) ? topk_sliced_len(rows, p.kv_len, p.topk) : 0;
   f.cand_bytes = 0;
   if (f.tk_sl_len > 0) {
     size_t hist_bytes;

@@ -68,7 +68,10 @@ struct AttnLaunch {
   int out_f32;             // out dtype: 1 fp32, 0 bf16
 };
 
-// Indexer.  *_bf16 / *_fp8 need H = 64, D = 128.
+// Indexer.  *_bf16 / *_fp8 need H = 64, D = 128.  Launches of at most
+// kDecodeIndexQueries queries per sequence run the decode kernel, the only
+// one that clears zero_hist (the others refuse it).
+constexpr int kDecodeIndexQueries = 4;
 hipError_t launch_index_f32(const IndexLaunch& a, hipStream_t s);
 hipError_t launch_index_bf16(const IndexLaunch& a, hipStream_t s);
 hipError_t launch_index_fp8(const IndexLaunch& a, hipStream_t s);

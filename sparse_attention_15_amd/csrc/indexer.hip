@@ -470,10 +470,11 @@ int pick_ksplit(int blocks, int ntiles_max) {
 
 template <bool FP8>
 hipError_t launch_mfma(const IndexLaunch& a, hipStream_t s) {
-  if (a.q_count <= 4) {
+  if (a.q_count <= kDecodeIndexQueries) {
     dim3 grid((a.Lk + kDecChunk - 1) / kDecChunk, a.B * a.q_count);
     hipLaunchKernelGGL(idx_decode_kernel<FP8>, grid, dim3(256), 0, s, a);
   } else {
+    if (a.zero_hist) return hipErrorInvalidValue;   // only the decode kernel clears it
     constexpr int QB = 8;
     const int nqb = (a.q_count + QB - 1) / QB;
     const int n_max = a.Lk - a.Lq + a.q_begin + a.q_count;
@@ -487,6 +488,7 @@ hipError_t launch_mfma(const IndexLaunch& a, hipStream_t s) {
 }  // namespace
 
 hipError_t launch_index_f32(const IndexLaunch& a, hipStream_t s) {
+  if (a.zero_hist) return hipErrorInvalidValue;   // only the decode kernel clears it
   dim3 grid((a.Lk + 255) / 256, a.B * a.q_count);
   const size_t smem = (size_t)(a.H * a.D + a.H) * sizeof(float);
   hipLaunchKernelGGL(idx_f32_kernel, grid, dim3(256), smem, s, a);
