@@ -50,6 +50,7 @@ KERNELS = {
     "idx_prefill_kernel": ("indexer.hip", 0),
     "idx_f32_kernel": ("indexer.hip", 0),
     "topk_kernel": ("topk.hip", 1),
+    "topk_cand_kernel": ("topk.hip", 1),
     "tk_coop_kernel": ("topk_sliced.hip", 1),
     "tk_hist_kernel + tk_classify_kernel + tk_emit_kernel": ("topk_sliced.hip", 1),
     "attn_bf16_kernel": ("sparse_mla.hip", 2),
@@ -77,16 +78,20 @@ def measured_traffic(kernel, workload):
     return rec.get("bytes_per_launch")
 
 
-def stage_kernels(cfg, slice_len=0):
+def stage_kernels(cfg, slice_len=0, list_slots=0):
     """Kernel that runs in each stage of dsa_forward for this workload.
 
-    slice_len > 0: the top-k cuts each row into slices of that many positions,
-    one work-group each; all slices of the launch run together in one
-    cooperative kernel when they fit on the chip at once (256 CUs hold at
-    least one work-group each), else in three kernels."""
+    list_slots > 0: the top-k selects from the indexer's per-chunk candidate
+    lists (one work-group per row).  slice_len > 0: the top-k cuts each row
+    into slices of that many positions, one work-group each; all slices of
+    the launch run together in one cooperative kernel when they fit on the
+    chip at once (256 CUs hold at least one work-group each), else in three
+    kernels."""
     decode = cfg.q_len <= 4
     topk = "topk_kernel"
-    if slice_len > 0:
+    if list_slots > 0:
+        topk = "topk_cand_kernel"
+    elif slice_len > 0:
         slices = cfg.batch * cfg.q_len * -(-cfg.kv_len // slice_len)
         topk = "tk_coop_kernel" if slices <= 256 else "tk_hist_kernel + tk_classify_kernel + tk_emit_kernel"
     if cfg.index_dtype == "f32":
@@ -107,7 +112,7 @@ def kernel_units(cfg, kernel, al, n_chunks, split_rows):
         peak = MFMA_FP8_PEAK_TFLOPS if cfg.index_dtype == "fp8_e4m3" else MFMA_BF16_PEAK_TFLOPS
         return ("mfma", al["index_flops"] / n_chunks, "TFLOP/s", peak,
                 "algorithmic flops per launch: 2*H*D per visible (query, key) pair")
-    if kernel == "topk_kernel" or kernel.startswith("tk_"):
+    if kernel.startswith("topk_") or kernel.startswith("tk_"):
         return ("hbm", 4 * al["pairs"] / n_chunks, "GB/s", HBM_PEAK_GBS,
                 "algorithmic bytes per launch: one fp32 score per visible (query, key) pair")
     if kernel.startswith("attn_") and kernel != "attn_combine_kernel":
@@ -503,7 +508,7 @@ def main():
     al = algorithmic(cfg)
     ms_per_step = elapsed * 1e3 / args.steps
     qps = cfg.batch * cfg.q_len / (ms_per_step * 1e-3)
-    kernels = stage_kernels(cfg, dsa.topk_slice_len(p))
+    kernels = stage_kernels(cfg, dsa.topk_slice_len(p), dsa.topk_list_slots(p))
     splits = dsa.attn_splits(p)
     dom = max(range(dsa.DSA_NUM_STAGES), key=lambda st: stage_ms[st])
     kname = kernels[dom]

@@ -48,7 +48,7 @@
 extern "C" {
 #endif
 
-#define DSA_ABI_VERSION 5
+#define DSA_ABI_VERSION 6
 #define DSA_MAX_KV_LEN_BF16 1864135   /* (2^31 - 1) / 1152 */
 
 typedef enum {
@@ -331,6 +331,20 @@ int32_t dsa_forward_attn_splits(const dsa_problem_t* prob);
  * several work-groups select from together), or 0 when each row is selected
  * by one work-group (or the problem is invalid).  Host only. */
 int32_t dsa_forward_topk_slice_len(const dsa_problem_t* prob);
+
+/* List slots per 2048-key chunk of the filtered top-k dsa_forward uses for
+ * this problem, or 0 when it selects from the full score rows (or the
+ * problem is invalid).  Host only.  With decode-shaped launches of 16 or
+ * more chunks per row, the indexer kernel also lists each chunk's
+ * highest-scoring keys: every key whose 12-bit key prefix lies above a
+ * cutoff bin that leaves at most this many keys.  The top-k then selects
+ * from the lists alone whenever the K-th largest listed key lies above
+ * every chunk's cutoff (then every key of the row at least as large is
+ * listed); otherwise it selects from the full row.  The result is the
+ * exact top-k either way (HF model doc "DeepSeek-V3.2", section "DeepSeek
+ * Sparse Attention (DSA)", item 2: each query keeps its index_topk
+ * best-scoring positions). */
+int32_t dsa_forward_topk_list_slots(const dsa_problem_t* prob);
 
 /* Static description of a status code. */
 const char* dsa_status_string(dsa_status_t status);

@@ -4,7 +4,7 @@ exact top-k and sparse MLA attention, behind the C ABI in include/dsa.h.
 The Python layer only marshals torch tensors to the library; see dsa.py.
 """
 from .dsa import (  # noqa: F401
-    DSAError, Problem, StageEvents, abi_version, attn_splits, cache_append, topk_slice_len, forward, forward_chunks, forward_static,
+    DSAError, Problem, StageEvents, abi_version, attn_splits, cache_append, topk_slice_len, topk_list_slots, forward, forward_chunks, forward_static,
     index_rotate_quantize, index_q_proj, head_weights_proj, head_weights_workspace_size, out_unabsorb,
     index_scores, lib,
     make_problem, sparse_mla_attn, status_string, topk, workspace_size,

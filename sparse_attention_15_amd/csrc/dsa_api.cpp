@@ -80,6 +80,7 @@ struct ForwardPlan {
   int chunk;       // queries per chunk
   int n_chunks;
   int tk_sl_len;                 // sliced top-k: positions per work-group (0 = not used)
+  int tk_cand_m;                 // filtered top-k: list slots per chunk (0 = not used)
   size_t scores_bytes, idx_bytes, part_bytes, cand_bytes;
   size_t total() const { return scores_bytes + idx_bytes + part_bytes + cand_bytes; }
 };
@@ -92,11 +93,18 @@ ForwardPlan plan_forward(const dsa_problem_t& p, Path path, bool need_idx) {
   f.idx_bytes = need_idx ? align_up((size_t)p.batch * p.q_len * p.topk * 4) : 0;
   const int rows = p.batch * f.chunk;
   f.part_bytes = attn_partials_bytes(p, rows, attn_splits(p, path, rows));
-  // few decode-shaped rows (the decode indexer kernel zeroes the histogram
-  // the sliced selection accumulates into): one work-group per row slice
-  f.tk_sl_len = (path != kPathF32 && f.chunk <= kDecodeIndexQueries) ? topk_sliced_len(rows, p.kv_len, p.topk) : 0;
+  // Decode-shaped rows (the decode indexer kernel runs): with enough
+  // 2048-key chunks the indexer lists each chunk's candidates and top-k
+  // selects from the lists; else few long rows take one work-group per row
+  // slice (the decode indexer zeroes the histogram the sliced selection
+  // accumulates into).
+  const bool decode = path != kPathF32 && f.chunk <= kDecodeIndexQueries;
+  f.tk_cand_m = decode ? topk_cand_m(p.kv_len, p.topk) : 0;
+  f.tk_sl_len = (decode && f.tk_cand_m == 0) ? topk_sliced_len(rows, p.kv_len, p.topk) : 0;
   f.cand_bytes = 0;
-  if (f.tk_sl_len > 0) {
+  if (f.tk_cand_m > 0) {
+    f.cand_bytes = align_up(topk_cand_bytes(rows, p.kv_len));
+  } else if (f.tk_sl_len > 0) {
     size_t hist_bytes;
     f.cand_bytes = align_up(topk_sliced_bytes(rows, p.kv_len, f.tk_sl_len, &hist_bytes));
   }
@@ -116,6 +124,22 @@ void carve_sliced(TopkLaunch& ta, char* base, int rows, int n_max, int L) {
   ta.sl_cand = ta.sl_list + (size_t)rows * ta.sl_count * L * 2;
 }
 
+// Workspace pieces of the filtered top-k's candidate lists, in the order
+// topk_cand_bytes counts them: keys, positions within the chunk, headers.
+void carve_cand(IndexLaunch& ia, TopkLaunch& ta, char* base, int rows, int n_max, int m) {
+  const int nch = (n_max + kCandChunk - 1) / kCandChunk;
+  const size_t lists = (size_t)rows * nch;
+  ia.cand_keys = reinterpret_cast<uint32_t*>(base);
+  ia.cand_offs = reinterpret_cast<uint16_t*>(base + lists * kCandCap * 4);
+  ia.cand_hdr = reinterpret_cast<int32_t*>(base + lists * kCandCap * 6);
+  ia.cand_m = m;
+  ta.cand_keys = ia.cand_keys;
+  ta.cand_offs = ia.cand_offs;
+  ta.cand_hdr = ia.cand_hdr;
+  ta.cand_chunks = nch;
+  ta.cand_m = m;
+}
+
 IndexLaunch make_index(const dsa_problem_t& p, const void* q, const uint8_t* qs, const void* k, const uint8_t* ks,
                        const float* w, float* scores, int64_t row_stride, int q_begin, int q_count, int masked) {
   IndexLaunch a;
@@ -125,6 +149,7 @@ IndexLaunch make_index(const dsa_problem_t& p, const void* q, const uint8_t* qs,
   a.Lc = p.kv_capacity ? p.kv_capacity : p.kv_len;
   a.q_begin = q_begin; a.q_count = q_count; a.write_masked = masked;
   a.zero_hist = nullptr;
+  a.cand_keys = nullptr; a.cand_offs = nullptr; a.cand_hdr = nullptr; a.cand_m = 0;
   return a;
 }
 
@@ -137,6 +162,7 @@ TopkLaunch make_topk(const dsa_problem_t& p, const float* scores, int64_t row_st
   a.vec_ok = aligned16(scores) && (row_stride % 4) == 0;
   a.sl_len = 0; a.sl_count = 0; a.sl_hist = nullptr; a.sl_info = nullptr; a.sl_rowinfo = nullptr;
   a.sl_list = nullptr; a.sl_cand = nullptr;
+  a.cand_keys = nullptr; a.cand_offs = nullptr; a.cand_hdr = nullptr; a.cand_chunks = 0; a.cand_m = 0;
   return a;
 }
 
@@ -221,7 +247,9 @@ dsa_status_t forward_impl(const dsa_problem_t* prob, const void* q_idx, const ui
     if ((e = ev.rec(c, 0, 0)) != hipSuccess) return DSA_ERR_HIP;
     IndexLaunch ia = make_index(p, q_idx, q_scale, k_idx, k_scale, head_w, scores, p.kv_len, q0, qn, 0);
     TopkLaunch ta = make_topk(p, scores, p.kv_len, idx, q0, qn);
-    if (f.tk_sl_len > 0) {
+    if (f.tk_cand_m > 0) {
+      carve_cand(ia, ta, reinterpret_cast<char*>(cand), p.batch * f.chunk, p.kv_len, f.tk_cand_m);
+    } else if (f.tk_sl_len > 0) {
       carve_sliced(ta, reinterpret_cast<char*>(cand), p.batch * f.chunk, p.kv_len, f.tk_sl_len);
       ia.zero_hist = ta.sl_hist;
     }
@@ -229,7 +257,9 @@ dsa_status_t forward_impl(const dsa_problem_t* prob, const void* q_idx, const ui
     if ((e = ev.rec(c, 0, 1)) != hipSuccess) return DSA_ERR_HIP;
     // 2. top-k
     if ((e = ev.rec(c, 1, 0)) != hipSuccess) return DSA_ERR_HIP;
-    e = f.tk_sl_len > 0 ? launch_topk_sliced(ta, false, stream) : launch_topk(ta, stream);
+    e = f.tk_cand_m > 0   ? launch_topk_cand(ta, stream)
+        : f.tk_sl_len > 0 ? launch_topk_sliced(ta, false, stream)
+                          : launch_topk(ta, stream);
     if (e != hipSuccess) return hip_status(e);
     if ((e = ev.rec(c, 1, 1)) != hipSuccess) return DSA_ERR_HIP;
     // 3. attention (+ combine); every chunk uses the split count the
@@ -519,6 +549,12 @@ int32_t dsa_forward_topk_slice_len(const dsa_problem_t* prob) {
   Path path;
   if (check_problem(prob, &path) != DSA_OK) return 0;
   return plan_forward(*prob, path, true).tk_sl_len;
+}
+
+int32_t dsa_forward_topk_list_slots(const dsa_problem_t* prob) {
+  Path path;
+  if (check_problem(prob, &path) != DSA_OK) return 0;
+  return plan_forward(*prob, path, true).tk_cand_m;
 }
 
 const char* dsa_status_string(dsa_status_t s) {

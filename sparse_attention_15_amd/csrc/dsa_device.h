@@ -132,6 +132,18 @@ __device__ __forceinline__ void lds_dma_u8(const void* gbase, uint32_t voff, uin
 }
 #pragma clang diagnostic pop
 
+// Order-preserving 32-bit key of a score, as the top-k kernels rank them:
+// larger score, larger key; -0.0 maps like +0.0.  Key 0 is reserved for
+// "no element" (slots past a row's end): real scores map to >= 1 (only the
+// all-ones NaN pattern would map to 0, and NaN scores have no defined place
+// in the order).
+__device__ __forceinline__ uint32_t order_key(float x) {
+  uint32_t u = __builtin_bit_cast(uint32_t, x);
+  if (u == 0x80000000u) u = 0u;                 // -0.0 == +0.0
+  const uint32_t k = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  return k > 1u ? k : 1u;
+}
+
 // ue8m0 exponent byte -> 2^(e-127) as fp32 (e = 0 gives 2^-127, a subnormal).
 __device__ __forceinline__ float ue8m0_to_f32(uint32_t e) {
   return e == 0 ? __builtin_bit_cast(float, 0x00400000u) : __builtin_bit_cast(float, e << 23);

@@ -23,7 +23,24 @@ struct IndexLaunch {
   int write_masked;        // also write -inf for positions beyond the causal limit
   uint32_t* zero_hist;     // decode shape only: rows x kTopkRowHeadWords words set to
                            // zero for the sliced top-k that follows (null: none)
+  // Decode shape only: per-chunk candidate lists for the filtered top-k
+  // (cand_m = 0: none).  Chunk c of a row covers keys [kCandChunk c,
+  // kCandChunk (c + 1)); its list holds, in position order, every visible
+  // key of the chunk whose 12-bit key prefix exceeds the chunk's cutoff bin
+  // (at most cand_m of them; cutoff -1: every visible key).
+  //   cand_keys [rows][chunks][kCandCap]  order keys
+  //   cand_offs [rows][chunks][kCandCap]  positions within the chunk
+  //   cand_hdr  [rows][chunks][2]         (count, cutoff bin)
+  uint32_t* cand_keys;
+  uint16_t* cand_offs;
+  int32_t* cand_hdr;
+  int cand_m;
 };
+
+// Candidate lists of the filtered decode top-k.
+constexpr int kCandChunk = 2048;  // keys per list (the decode indexer's work-group chunk)
+constexpr int kCandCap = 256;     // list slots per chunk
+constexpr int kCandMax = 8192;    // candidate slots per row (chunks x cand_m)
 
 struct TopkLaunch {
   const float* scores;     // rows as above
@@ -43,6 +60,12 @@ struct TopkLaunch {
   int32_t* sl_rowinfo;
   uint32_t* sl_list;
   uint32_t* sl_cand;
+  // filtered selection (launch_topk_cand): the decode indexer's candidate
+  // lists (see IndexLaunch), cand_chunks per row, cand_m slots used per chunk
+  const uint32_t* cand_keys;
+  const uint16_t* cand_offs;
+  const int32_t* cand_hdr;
+  int cand_chunks, cand_m;
 };
 
 constexpr int kMaxTopkSlices = 512;
@@ -99,6 +122,12 @@ int topk_sliced_len(int rows, int n_max, int K);
 size_t topk_sliced_bytes(int rows, int n_max, int L, size_t* hist_bytes);
 // zero_hist: clear the histogram first (else the caller's earlier kernel did).
 hipError_t launch_topk_sliced(const TopkLaunch& a, bool zero_hist, hipStream_t s);
+// Filtered top-k from the decode indexer's per-chunk candidate lists: list
+// slots per chunk (cand_m) for rows of up to n_max positions, or 0 when the
+// lists would not hold a safe margin over a chunk's share of the K chosen.
+int topk_cand_m(int n_max, int K);
+size_t topk_cand_bytes(int rows, int n_max);
+hipError_t launch_topk_cand(const TopkLaunch& a, hipStream_t s);
 
 // Sparse MLA.  *_bf16 needs NH = 128, Dqk = 576, Dv = 512.
 hipError_t launch_attn_f32(const AttnLaunch& a, hipStream_t s);

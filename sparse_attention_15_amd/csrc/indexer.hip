@@ -195,6 +195,112 @@ __device__ __forceinline__ float reduce4(float p0, float p1, float p2, float p3)
   return __builtin_bit_cast(float, ta) + __builtin_bit_cast(float, tb);
 }
 
+// ------------------------------------------- decode: candidate lists -------
+// Inclusive scan over a wave's 64 lanes (DPP row shifts 1, 2, 4, 8, then the
+// row_bcast:15 and row_bcast:31 steps).
+template <int CTRL, int ROWS>
+__device__ __forceinline__ uint32_t dpp_shift(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, ROWS, 0xf, false);
+}
+__device__ __forceinline__ uint32_t wave_scan_incl(uint32_t v) {
+  v += dpp_shift<0x111, 0xf>(v);
+  v += dpp_shift<0x112, 0xf>(v);
+  v += dpp_shift<0x114, 0xf>(v);
+  v += dpp_shift<0x118, 0xf>(v);
+  v += dpp_shift<0x142, 0xa>(v);
+  v += dpp_shift<0x143, 0xc>(v);
+  return v;
+}
+
+// The chunk's candidate list for the filtered top-k (256 threads; the
+// chunk's nk scores in sc; hist: 4096 + 8 words of free LDS).  Every
+// visible key of the chunk whose 12-bit key prefix (sign, exponent, three
+// mantissa bits) lies above the cutoff bin goes to the list, in position
+// order; the cutoff is the highest bin at which more than cand_m keys would
+// be listed (-1 when the chunk has at most cand_m keys).  The top-k then
+// only needs the lists: if the K-th largest listed key lies in a bin above
+// every chunk's cutoff, every key at least as large as it is listed, so the
+// lists hold the whole selection.
+__device__ void chunk_candidates(const IndexLaunch& a, int row, int nk, const float* sc, uint32_t* hist) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  uint32_t* red = hist + 4096;
+  const int M = a.cand_m;
+  const int64_t lst = (int64_t)row * gridDim.x + blockIdx.x;
+  // positions 8 tid .. 8 tid + 7 of the chunk
+  uint32_t k[8];
+  {
+    const f32x4 v0 = *reinterpret_cast<const f32x4*>(sc + 8 * tid);
+    const f32x4 v1 = *reinterpret_cast<const f32x4*>(sc + 8 * tid + 4);
+    const float v[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+#pragma unroll
+    for (int e = 0; e < 8; ++e) k[e] = 8 * tid + e < nk ? order_key(v[e]) : 0u;
+  }
+  int cut = -1;
+  if (nk > M) {                                  // uniform
+#pragma unroll
+    for (int q = 0; q < 4; ++q) st16(hist + 4 * (tid + 256 * q), u32x4{0u, 0u, 0u, 0u});
+    __syncthreads();
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+      if (k[e]) atomicAdd(&hist[k[e] >> 20], 1u);
+    __syncthreads();
+    // thread t holds bins 4095 - 16t - j, j = 0..15 (from the top down)
+    const int top = 4095 - 16 * tid;
+    uint32_t c[16];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const u32x4 h = *reinterpret_cast<const u32x4*>(hist + top - 4 * q - 3);
+      c[4 * q] = h.w;
+      c[4 * q + 1] = h.z;
+      c[4 * q + 2] = h.y;
+      c[4 * q + 3] = h.x;
+    }
+    uint32_t tot = 0u;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) tot += c[j];
+    const uint32_t incl = wave_scan_incl(tot);
+    if (lane == 63) red[4 + wave] = incl;
+    __syncthreads();
+    uint32_t run = incl - tot;                   // keys in the bins above mine
+    for (int w = 0; w < wave; ++w) run += red[4 + w];
+    if (run <= (uint32_t)M && run + tot > (uint32_t)M) {
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        if (run + c[j] > (uint32_t)M) {
+          red[0] = (uint32_t)(top - j);
+          break;
+        }
+        run += c[j];
+      }
+    }
+    __syncthreads();
+    cut = (int)red[0];
+  }
+  uint32_t take = 0u;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) take |= (k[e] != 0u && (int)(k[e] >> 20) > cut) ? (1u << e) : 0u;
+  const uint32_t cnt = __builtin_popcount(take);
+  const uint32_t incl = wave_scan_incl(cnt);
+  if (lane == 63) red[4 + wave] = incl;
+  __syncthreads();
+  uint32_t off = incl - cnt, total = 0u;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    off += w < wave ? red[4 + w] : 0u;
+    total += red[4 + w];
+  }
+  uint32_t* keys = a.cand_keys + lst * kCandCap;
+  uint16_t* offs = a.cand_offs + lst * kCandCap;
+#pragma unroll
+  for (int e = 0; e < 8; ++e)
+    if (take & (1u << e)) {
+      keys[off] = k[e];
+      offs[off] = (uint16_t)(8 * tid + e);
+      ++off;
+    }
+  if (tid == 0) *reinterpret_cast<int2*>(a.cand_hdr + 2 * lst) = int2{(int)total, cut};
+}
+
 // ------------------------------------------------------ decode shape -------
 // grid (ceil(Lk / 2048), B * q_count), 4 waves; the work-group walks the
 // 16-key tiles of keys [c0, c0 + 2048) of its query in order, tile t going
@@ -240,7 +346,11 @@ __global__ __launch_bounds__(256, 2) void idx_decode_kernel(IndexLaunch a) {
     for (int j = tid; j < kTopkRowHeadWords / 4; j += 256) h[j] = u32x4{0u, 0u, 0u, 0u};
     wait_vmcnt<0>();
   }
-  if (c0 >= cn) return;                          // uniform over the work-group
+  if (c0 >= cn) {                                // uniform over the work-group
+    if (a.cand_m && tid == 0)                     // no visible key: an empty list
+      *reinterpret_cast<int2*>(a.cand_hdr + 2 * ((int64_t)row * gridDim.x + blockIdx.x)) = int2{0, -1};
+    return;
+  }
   const int nk = cn - c0;
   const int ntile = (nk + TK - 1) / TK;
   const int nst = (ntile - wave + 3) / 4;        // my tiles: wave, wave + 4, ...
@@ -321,6 +431,9 @@ __global__ __launch_bounds__(256, 2) void idx_decode_kernel(IndexLaunch a) {
   // coalesced stores of the work-group's scores
   __syncthreads();
   for (int j = tid; j < nk; j += 256) out[c0 + j] = sc[j];
+  // the key rings are free now (every wave has passed its last stage)
+  static_assert(sizeof(ring) >= (4096 + 8) * 4, "the candidate histogram fits in the rings");
+  if (a.cand_m) chunk_candidates(a, row, nk, sc, reinterpret_cast<uint32_t*>(&ring[0][0][0]));
 }
 
 // ----------------------------------------------------- prefill shape -------
@@ -471,10 +584,14 @@ int pick_ksplit(int blocks, int ntiles_max) {
 template <bool FP8>
 hipError_t launch_mfma(const IndexLaunch& a, hipStream_t s) {
   if (a.q_count <= kDecodeIndexQueries) {
+    static_assert(kDecChunk == kCandChunk, "candidate lists follow the work-group chunks");
+    if (a.cand_m && (a.cand_m > kCandCap || (a.cand_m & 7) || !a.cand_keys || !a.cand_offs || !a.cand_hdr))
+      return hipErrorInvalidValue;
     dim3 grid((a.Lk + kDecChunk - 1) / kDecChunk, a.B * a.q_count);
     hipLaunchKernelGGL(idx_decode_kernel<FP8>, grid, dim3(256), 0, s, a);
   } else {
-    if (a.zero_hist) return hipErrorInvalidValue;   // only the decode kernel clears it
+    // only the decode kernel clears zero_hist and writes candidate lists
+    if (a.zero_hist || a.cand_m) return hipErrorInvalidValue;
     constexpr int QB = 8;
     const int nqb = (a.q_count + QB - 1) / QB;
     const int n_max = a.Lk - a.Lq + a.q_begin + a.q_count;
@@ -488,7 +605,7 @@ hipError_t launch_mfma(const IndexLaunch& a, hipStream_t s) {
 }  // namespace
 
 hipError_t launch_index_f32(const IndexLaunch& a, hipStream_t s) {
-  if (a.zero_hist) return hipErrorInvalidValue;   // only the decode kernel clears it
+  if (a.zero_hist || a.cand_m) return hipErrorInvalidValue;   // decode kernel only
   dim3 grid((a.Lk + 255) / 256, a.B * a.q_count);
   const size_t smem = (size_t)(a.H * a.D + a.H) * sizeof(float);
   hipLaunchKernelGGL(idx_f32_kernel, grid, dim3(256), smem, s, a);

@@ -589,23 +589,24 @@ __global__ __launch_bounds__(kWavesA * 64, 1) void attn_bf16_kernel(AttnLaunch a
 
 // Merge split partials: out = sum_s exp(lse_s - LSE) * O_s, LSE = log sum_s exp(lse_s).
 // The partials are in the attention kernel's register order (see its
-// epilogue).  grid (32, rows): work-group x covers heads 32w .. 32w+31
-// (w = x / 8) and value tiles 2vg, 2vg+1, i.e. dims 64vg .. 64vg+63
-// (vg = x % 8): a 4 KB (bf16) or 8 KB (fp32) block of each split's
-// partial.  Thread t takes that block's 16-byte-aligned pair of lanes
-// 2t, 2t+1 (two heads, four dims each), loads it for G splits at a time
-// (all in flight together), adds the splits in order with fp32 weights and
-// stores its two 4-dim pieces.  The 32 heads' weights come from their LSEs
-// while the partials load.
-constexpr int kCombVT = 2;                        // value tiles per combine work-group
-template <int S, bool F32>
-__global__ __launch_bounds__(256) void attn_combine_kernel(AttnLaunch a) {
+// epilogue).  grid (4 * 16 / VT, rows): work-group x covers heads 32w ..
+// 32w+31 (w = x / (16 / VT)) and VT value tiles from VT vg (vg = x % (16 /
+// VT)), i.e. 32 VT dims: a 2 VT KB (bf16) or 4 VT KB (fp32) block of each
+// split's partial.  Thread t takes that block's 16-byte-aligned pair of
+// lanes 2t, 2t+1 (two heads, four dims each), loads it for G splits at a
+// time (all in flight together), adds the splits in order with fp32
+// weights and stores its two 4-dim pieces.  The 32 heads' weights come from
+// their LSEs while the partials load.  Few rows take VT = 1 (twice the
+// work-groups, every split in flight at once for bf16).
+template <int S, bool F32, int VT>
+__global__ __launch_bounds__(128 * VT) void attn_combine_kernel(AttnLaunch a) {
   constexpr bool PF32 = kF32Partials || F32;      // partial precision
   constexpr int EB = PF32 ? 4 : 2;                // bytes per partial value
   constexpr int OB = F32 ? 4 : 2;                 // bytes per output value
   constexpr int LD = 2 * 4 * EB / 16;             // 16-byte loads per thread and split
-  constexpr int G = (PF32 ? 8 : 16) < S ? (PF32 ? 8 : 16) : S;   // splits in flight at once
-  constexpr int NVG = kVTiles / kCombVT;          // work-groups per 32 heads
+  constexpr int GM = VT == 1 ? (PF32 ? 16 : 32) : (PF32 ? 8 : 16);
+  constexpr int G = GM < S ? GM : S;              // splits in flight at once
+  constexpr int NVG = kVTiles / VT;               // work-groups per 32 heads
   __shared__ float wt[S][32];
   int gx = blockIdx.x, rr = blockIdx.y;
   if ((gridDim.y & 7) == 0) {                     // row rr on the XCD its splits ran on
@@ -621,7 +622,7 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnLaunch a) {
   const int64_t qrow = (int64_t)b * a.Lq + i;
   // this thread's lanes l0, l0+1 of block (w, vt, q) of every split
   const int c = 2 * tid;                          // chunk within the 512 chunks of (w, vg)
-  const int vt = kCombVT * vg + (c >> 8), q = (c >> 6) & 3, l0 = c & 63;
+  const int vt = VT * vg + (c >> 8), q = (c >> 6) & 3, l0 = c & 63;
   const int64_t split_u4 = (int64_t)NH * a.Dv * EB / 16;          // 16-byte units per split
   const u32x4* src = static_cast<const u32x4*>(a.part_o) + (int64_t)rr * S * split_u4 +
                      ((((int64_t)w * kVTiles + vt) * 4 + q) * 64 + l0) * (4 * EB) / 16;
@@ -766,6 +767,8 @@ __global__ __launch_bounds__(256) void attn_f32_kernel(AttnLaunch a) {
 
 }  // namespace
 
+constexpr int kCombFewRows = 16;
+
 int attn_splits_bf16(int rows, int K) {
   // at least 128 keys (4 blocks) per split: a split's fixed costs (list, Q,
   // first gathers, epilogue) and its 128 KB of partials for the combine
@@ -791,19 +794,25 @@ hipError_t launch_attn_bf16(const AttnLaunch& a, hipStream_t s) {
   return hipGetLastError();
 }
 
-template <bool F32>
-hipError_t launch_combine_t(const AttnLaunch& a, hipStream_t s) {
-  dim3 grid(4 * (kVTiles / kCombVT), a.B * a.q_count);
-  dim3 block(256);
+template <bool F32, int VT>
+hipError_t launch_combine_vt(const AttnLaunch& a, hipStream_t s) {
+  dim3 grid(4 * (kVTiles / VT), a.B * a.q_count);
+  dim3 block(128 * VT);
   switch (a.splits) {
-    case 2: hipLaunchKernelGGL((attn_combine_kernel<2, F32>), grid, block, 0, s, a); break;
-    case 4: hipLaunchKernelGGL((attn_combine_kernel<4, F32>), grid, block, 0, s, a); break;
-    case 8: hipLaunchKernelGGL((attn_combine_kernel<8, F32>), grid, block, 0, s, a); break;
-    case 16: hipLaunchKernelGGL((attn_combine_kernel<16, F32>), grid, block, 0, s, a); break;
-    case 32: hipLaunchKernelGGL((attn_combine_kernel<32, F32>), grid, block, 0, s, a); break;
+    case 2: hipLaunchKernelGGL((attn_combine_kernel<2, F32, VT>), grid, block, 0, s, a); break;
+    case 4: hipLaunchKernelGGL((attn_combine_kernel<4, F32, VT>), grid, block, 0, s, a); break;
+    case 8: hipLaunchKernelGGL((attn_combine_kernel<8, F32, VT>), grid, block, 0, s, a); break;
+    case 16: hipLaunchKernelGGL((attn_combine_kernel<16, F32, VT>), grid, block, 0, s, a); break;
+    case 32: hipLaunchKernelGGL((attn_combine_kernel<32, F32, VT>), grid, block, 0, s, a); break;
     default: return hipErrorInvalidValue;       // splits are powers of two up to 32
   }
   return hipGetLastError();
+}
+
+template <bool F32>
+hipError_t launch_combine_t(const AttnLaunch& a, hipStream_t s) {
+  // fewer than 16 rows: 64 work-groups per row instead of 32
+  return a.B * a.q_count < kCombFewRows ? launch_combine_vt<F32, 1>(a, s) : launch_combine_vt<F32, 2>(a, s);
 }
 
 // bf16 kernel shapes only: NH = 128, Dv = 512 (the attention kernel's register order)

@@ -41,17 +41,6 @@ constexpr int kWaves = kThreads / 64;
 constexpr int kBins = 4096;
 constexpr int kGroup = 8;            // chunks per emission group
 
-// Key 0 is reserved for positions that hold no element (the tail of the
-// last 16-byte chunk, unused candidate slots); real elements map to >= 1
-// (only the all-ones NaN pattern would map to 0, and NaN scores have no
-// defined place in the order).
-__device__ __forceinline__ uint32_t order_key(float x) {
-  uint32_t u = __builtin_bit_cast(uint32_t, x);
-  if (u == 0x80000000u) u = 0u;                 // -0.0 == +0.0
-  const uint32_t k = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-  return k > 1u ? k : 1u;
-}
-
 // DPP source shift (lanes whose source is out of range read 0).
 template <int CTRL, int ROWS>
 __device__ __forceinline__ uint32_t dpp(uint32_t v) {
@@ -154,15 +143,13 @@ __device__ void find_bin(Shared<NC, C>& sh, const uint32_t* h, int nb, uint32_t 
   __syncthreads();
 }
 
-// NC 16-byte chunks per thread kept in registers (0 = re-read each pass);
-// C histogram copies.
+// Selection of one row by the work-group (all threads call).  NC 16-byte
+// chunks per thread kept in registers (0 = re-read each pass); C histogram
+// copies.
 template <int NC, int C>
-__global__ __launch_bounds__(kThreads, NC == 2 ? 8 : 4) void topk_kernel(TopkLaunch a) {
-  __shared__ Shared<NC, C> sh;
+__device__ __forceinline__ void topk_row(Shared<NC, C>& sh, const TopkLaunch& a, int row) {
   constexpr int S = Shared<NC, C>::kStride;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int r = gridDim.x - 1 - blockIdx.x;       // longest rows first
-  const int row = r;
   const int b = row / a.q_count;
   const int i = a.q_begin + row % a.q_count;
   const int n_row = a.Lk - a.Lq + i + 1;          // visible keys of this query
@@ -528,6 +515,182 @@ __global__ __launch_bounds__(kThreads, NC == 2 ? 8 : 4) void topk_kernel(TopkLau
   }
 }
 
+template <int NC, int C>
+__global__ __launch_bounds__(kThreads, NC == 2 ? 8 : 4) void topk_kernel(TopkLaunch a) {
+  __shared__ Shared<NC, C> sh;
+  topk_row<NC, C>(sh, a, gridDim.x - 1 - blockIdx.x);   // longest rows first
+}
+
+// Filtered selection from the decode indexer's per-chunk candidate lists
+// (see chunk_candidates in the indexer).  Thread t takes list slots 8t ..
+// 8t + 7 of the row (chunk-major, so slot order is position order), keys 0
+// past each list's count.  A radix select over the listed keys finds their
+// K-th largest, T'.  When T''s 12-bit prefix lies above every chunk's cutoff
+// bin, every key >= T' of the row is listed, so T' is the row's K-th largest
+// key and the listed keys alone decide the selection; the chosen positions
+// then leave in slot order.  Otherwise (or with fewer than K keys listed)
+// the work-group selects from the full row of scores, NCF chunks per thread
+// in registers.
+template <int NCF>
+__global__ __launch_bounds__(kThreads, 4) void topk_cand_kernel(TopkLaunch a) {
+  constexpr int C = 8;
+  __shared__ Shared<NCF, C> sh;
+  __shared__ uint32_t s_total;
+  __shared__ int s_cut;
+  constexpr int S = Shared<NCF, C>::kStride;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int row = gridDim.x - 1 - blockIdx.x;
+  const int b = row / a.q_count;
+  const int i = a.q_begin + row % a.q_count;
+  const int n = a.Lk - a.Lq + i + 1;
+  const int K = a.K;
+  int32_t* out = a.out + ((int64_t)b * a.Lq + i) * K;
+  if (n <= K) {                                   // every visible position, then -1
+    for (int j = tid; j < K; j += kThreads) out[j] = j < n ? j : -1;
+    return;
+  }
+  const int M = a.cand_m, nch = a.cand_chunks;
+  const int s0 = 8 * tid;                         // my first slot
+  const bool act = s0 < nch * M;
+  const int ch = act ? s0 / M : 0;
+  const int sl = s0 - ch * M;                     // slot within the chunk's list
+  const int64_t lst = (int64_t)row * nch + ch;
+  uint32_t keys[2][4];
+  uint32_t offs[4];
+  int2 hd = int2{0, -1};
+  if (act) {
+    const u32x4 k0 = ld16(a.cand_keys + lst * kCandCap + sl);
+    const u32x4 k1 = ld16(a.cand_keys + lst * kCandCap + sl + 4);
+    const u32x4 o = ld16(a.cand_offs + lst * kCandCap + sl);
+    hd = *reinterpret_cast<const int2*>(a.cand_hdr + 2 * lst);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      keys[0][e] = k0[e];
+      keys[1][e] = k1[e];
+      offs[e] = o[e];
+    }
+  } else {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) keys[0][e] = keys[1][e] = offs[e] = 0u;
+  }
+  // pass 1 histograms (CC copies: a few thousand keys contend little), pass
+  // 3's, and the two row-wide figures, cleared while the lists load
+  constexpr int CC = 2;
+  const uint32_t copy_base = (uint32_t)(lane & (CC - 1)) * S;
+  for (int j = tid; j < CC * kBins / 4; j += kThreads) {
+    const int r = j / (kBins / 4), o = j - r * (kBins / 4);
+    st16(&sh.hist[r * S + 4 * o], u32x4{0u, 0u, 0u, 0u});
+  }
+  if (tid < 64) st16(&sh.h3[4 * tid], u32x4{0u, 0u, 0u, 0u});
+  if (tid == 0) {
+    s_total = 0u;
+    s_cut = -1;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int c = 0; c < 2; ++c)
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      if (sl + 4 * c + e >= hd.x) keys[c][e] = 0u;
+  uint32_t mine = 0u;
+#pragma unroll
+  for (int c = 0; c < 2; ++c)
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      if (keys[c][e]) {
+        atomicAdd(&sh.hist[copy_base + (keys[c][e] >> 20)], 1u);
+        ++mine;
+      }
+  {
+    const uint32_t incl = wave_incl_scan(mine);
+    if (lane == 63 && incl) atomicAdd(&s_total, incl);
+  }
+  if (act && sl == 0 && hd.y >= 0) atomicMax(&s_cut, hd.y);   // one thread per chunk
+  __syncthreads();
+  const uint32_t total = s_total;
+  const int cut = s_cut;
+  bool ok = total >= (uint32_t)K;                 // uniform
+  uint32_t prefix = 0, mask = 0, k_rem = (uint32_t)K;
+  bool whole = false;
+  if (ok) {
+    find_bin<CC, true>(sh, sh.hist, kBins, k_rem);
+    ok = (int)sh.bin > cut;
+    const uint32_t cnt = sh.cnt;
+    k_rem -= sh.above;
+    prefix = sh.bin << 20;
+    mask = 0xfff00000u;
+    whole = cnt == k_rem;
+  }
+  if (!ok) {
+    topk_row<NCF, C>(sh, a, row);                 // every thread takes this branch
+    return;
+  }
+  if (!whole) {
+    for (int pass = 1; pass < 3; ++pass) {
+      const int sh_ = pass == 1 ? 8 : 0;
+      const int nb = pass == 1 ? kBins : 256;
+      uint32_t* const h = pass == 1 ? sh.hist : sh.h3;
+#pragma unroll
+      for (int c = 0; c < 2; ++c)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (keys[c][e] != 0u && (keys[c][e] & mask) == prefix)
+            atomicAdd(&h[(keys[c][e] >> sh_) & (nb - 1)], 1u);
+      __syncthreads();
+      find_bin<1, false>(sh, h, nb, k_rem);
+      const uint32_t cnt = sh.cnt;
+      k_rem -= sh.above;
+      prefix |= sh.bin << sh_;
+      mask |= (uint32_t)(nb - 1) << sh_;
+      if (cnt == k_rem) {                         // the whole bin is taken
+        whole = true;
+        break;
+      }
+    }
+  }
+  // Emission in slot (= position) order: a block-wide scan of each thread's
+  // packed (above, equal) counts; equal keys are taken while fewer than
+  // k_rem came before (all of them when the last bin is taken whole).
+  const uint32_t quota = whole ? 0xffffffffu : k_rem;
+  uint32_t pk = 0u;
+#pragma unroll
+  for (int c = 0; c < 2; ++c)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const uint32_t k = keys[c][e], m = k & mask;
+      pk += (k != 0u && m > prefix) ? 1u : 0u;
+      pk += (k != 0u && m == prefix) ? 0x10000u : 0u;
+    }
+  const uint32_t incl = wave_incl_scan(pk);
+  if (lane == 63) sh.wsum[wave] = incl;
+  __syncthreads();
+  const uint32_t excl = incl - pk + sum_before(sh.wsum, wave);
+  uint32_t g_b = excl & 0xffffu, e_b = excl >> 16;
+  const int pos0 = ch * kCandChunk;
+#pragma unroll
+  for (int c = 0; c < 2; ++c)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const uint32_t k = keys[c][e], m = k & mask;
+      const bool gt = k != 0u && m > prefix, eq = k != 0u && m == prefix;
+      if (gt || (eq && e_b < quota)) {
+        const uint32_t slot = g_b + min(e_b, quota);
+        const int q = 4 * c + e;
+        const int pos = pos0 + (int)((offs[q >> 1] >> (16 * (q & 1))) & 0xffffu);
+        if (slot < (uint32_t)K) sh.hist[slot] = (uint32_t)pos;   // always, by construction
+      }
+      g_b += gt ? 1u : 0u;
+      e_b += eq ? 1u : 0u;
+    }
+  __syncthreads();
+  if ((K & 3) == 0 && (reinterpret_cast<uintptr_t>(out) & 15u) == 0) {
+    for (int j = tid; j < K / 4; j += kThreads)
+      st16(out + 4 * j, u32x4{sh.hist[4 * j], sh.hist[4 * j + 1], sh.hist[4 * j + 2], sh.hist[4 * j + 3]});
+  } else {
+    for (int j = tid; j < K; j += kThreads) out[j] = (int32_t)sh.hist[j];
+  }
+}
+
 }  // namespace
 
 namespace {
@@ -553,6 +716,46 @@ void launch_rows(const TopkLaunch& a, int n_max, int grid, hipStream_t s) {
 }
 
 }  // namespace
+
+int topk_cand_m(int n_max, int K) {
+  // A chunk contributes about s = K / chunks of the chosen keys; with keys
+  // spread evenly its count varies by about sqrt(s).  Lists get a margin of
+  // 5 sqrt(s) + 16 keys over that share, so that their cutoff bins lie below
+  // the K-th largest score of the row: with 16 chunks of 2048 keys (32768
+  // positions) a chunk contributes about 128 keys and lists 256, a cutoff
+  // several 12-bit bins (an eighth of an octave each) below it for index
+  // scores.  A row whose chosen keys crowd into a few chunks falls back to
+  // the full selection, and so does any row the margin does not cover.
+  const int nch = (n_max + kCandChunk - 1) / kCandChunk;
+  if (nch < 16 || K > kThreads * 4) return 0;
+  int m = kCandMax / nch;
+  m = (m < kCandCap ? m : kCandCap) & ~7;
+  const double share = (double)K / nch;
+  return (m >= 8 && m >= share + 5.0 * __builtin_sqrt(share) + 16.0) ? m : 0;
+}
+
+size_t topk_cand_bytes(int rows, int n_max) {
+  const size_t lists = (size_t)rows * ((n_max + kCandChunk - 1) / kCandChunk);
+  return lists * kCandCap * 4 + lists * kCandCap * 2 + lists * 8;
+}
+
+hipError_t launch_topk_cand(const TopkLaunch& a, hipStream_t s) {
+  const int rows = a.B * a.q_count;
+  const int n_max = a.Lk - a.Lq + a.q_begin + a.q_count;
+  if (a.cand_m < 8 || (a.cand_m & 7) || a.cand_m > kCandCap || a.cand_chunks * a.cand_m > kCandMax ||
+      a.cand_chunks != (a.Lk + kCandChunk - 1) / kCandChunk || a.K > kThreads * 4 || !a.cand_keys ||
+      !a.cand_offs || !a.cand_hdr)
+    return hipErrorInvalidValue;
+  // the full-row fallback keeps rows of up to 65536 positions in registers
+  const int iters = ((n_max + 3) / 4 + kThreads - 1) / kThreads;
+  if (iters <= 8)
+    hipLaunchKernelGGL((topk_cand_kernel<8>), dim3(rows), dim3(kThreads), 0, s, a);
+  else if (iters <= 16)
+    hipLaunchKernelGGL((topk_cand_kernel<16>), dim3(rows), dim3(kThreads), 0, s, a);
+  else
+    hipLaunchKernelGGL((topk_cand_kernel<0>), dim3(rows), dim3(kThreads), 0, s, a);
+  return hipGetLastError();
+}
 
 hipError_t launch_topk(const TopkLaunch& a, hipStream_t s) {
   const int rows = a.B * a.q_count;

@@ -80,6 +80,8 @@ def lib() -> ctypes.CDLL:
     L.dsa_forward_attn_splits.restype = I32
     L.dsa_forward_topk_slice_len.argtypes = [P]
     L.dsa_forward_topk_slice_len.restype = I32
+    L.dsa_forward_topk_list_slots.argtypes = [P]
+    L.dsa_forward_topk_list_slots.restype = I32
     L.dsa_index_rotate_quantize.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_int32,
                                             ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
     L.dsa_index_rotate_quantize.restype = ctypes.c_int
@@ -225,8 +227,13 @@ def attn_splits(p: Problem) -> int:
 
 
 def topk_slice_len(p: Problem) -> int:
-    """Positions per work-group of forward's sliced top-k (0: one work-group per row)."""
+    """Positions per work-group of forward's sliced top-k (0: not used)."""
     return int(lib().dsa_forward_topk_slice_len(ctypes.byref(p)))
+
+
+def topk_list_slots(p: Problem) -> int:
+    """List slots per 2048-key chunk of forward's filtered top-k (0: not used)."""
+    return int(lib().dsa_forward_topk_list_slots(ctypes.byref(p)))
 
 
 def cache_append(p: Problem, k_new, k_new_scale, kv_new, k_idx, k_scale, kv):

@@ -37,7 +37,7 @@ def test_library_exports_every_declared_symbol(dsa):
     L = dsa.lib()
     for name in _declared_functions():
         assert hasattr(L, name), name
-    assert dsa.abi_version() == 5
+    assert dsa.abi_version() == 6
 
 
 def test_status_strings(dsa):
@@ -175,13 +175,33 @@ def test_sliced_topk_plan_is_host_only_and_bounded(dsa):
         # row head + per-slice counts + row info + a (key, position) pair and a key per position
         assert n >= batch * ((4096 + 64) * 4 + 512 * 8 + 16 + lk * 12), (batch, lk, k)
         assert n <= batch * ((4096 + 64) * 4 + 512 * 8 + 16 + (lk + 4096) * 12), (batch, lk, k)
-    # the forward's workspace covers its sliced selection
-    assert dsa.workspace_size(p4, dsa.DSA_OP_FORWARD) >= need
-    # the forward's plan query names the same choice: 4096 positions per
-    # work-group for 8 rows of 128K (32 slices each), none for 32 rows of 32K
-    assert dsa.topk_slice_len(p4) == 4096
+    # The forward's plan: decode rows of 16 or more 2048-key chunks select
+    # from the indexer's candidate lists (256 slots per chunk up to 32
+    # chunks, then as many as keep 8192 slots per row, when that leaves a
+    # margin over a chunk's share s of the K chosen: s + 5 sqrt(s) + 16);
+    # the sliced selection serves few long rows the lists do not.
+    assert dsa.topk_list_slots(p4) == 128
+    assert dsa.topk_list_slots(dsa.make_problem(C.DECODE_32K)) == 256
+    assert dsa.topk_list_slots(_prob(dsa, C.DECODE_32K, kv_len=65536)) == 256
+    assert dsa.topk_list_slots(_prob(dsa, C.DECODE_32K, kv_len=30720)) == 0      # 15 chunks
+    assert dsa.topk_list_slots(_prob(dsa, C.DECODE_32K, kv_len=30721)) == 256    # 16 chunks
+    assert dsa.topk_list_slots(_prob(dsa, C.DECODE_32K, topk=4097)) == 0        # share above 128
+    assert dsa.topk_list_slots(_prob(dsa, C.DECODE_128K, kv_len=262144)) == 64   # 128 chunks
+    assert dsa.topk_list_slots(_prob(dsa, C.DECODE_128K, kv_len=524288)) == 0    # 32 slots: no margin
+    assert dsa.topk_list_slots(_prob(dsa, C.DECODE_128K, kv_len=1864135)) == 0   # 911 chunks of 8
+    assert dsa.topk_list_slots(dsa.make_problem(C.PREFILL_8K)) == 0
+    assert dsa.topk_list_slots(dsa.make_problem(C.TINY)) == 0
+    assert dsa.topk_list_slots(_prob(dsa, C.DECODE_128K, q_len=0)) == 0
+    # lists: 256 keys, 256 positions and a header per chunk
+    assert dsa.workspace_size(p4, dsa.DSA_OP_FORWARD) >= 8 * 64 * (256 * 6 + 8)
+    assert dsa.topk_slice_len(p4) == 0
     assert dsa.topk_slice_len(dsa.make_problem(C.DECODE_32K)) == 0
-    assert dsa.topk_slice_len(_prob(dsa, C.DECODE_128K, batch=1)) == 1024
+    big_k = _prob(dsa, C.DECODE_128K, topk=8192)
+    assert dsa.topk_list_slots(big_k) == 0
+    # 4096 positions per work-group for 8 rows of 128K (32 slices each)
+    assert dsa.topk_slice_len(big_k) == 4096
+    assert dsa.workspace_size(big_k, dsa.DSA_OP_FORWARD) >= dsa.workspace_size(big_k, dsa.DSA_OP_TOPK)
+    assert dsa.topk_slice_len(_prob(dsa, C.DECODE_128K, batch=1, topk=8192)) == 1024
     assert dsa.topk_slice_len(_prob(dsa, C.DECODE_128K, q_len=0)) == 0
 
 

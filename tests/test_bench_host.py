@@ -39,8 +39,12 @@ def test_prefill_algorithmic_flops_by_hand():
     assert al["attn_flops"] == 2 * 128 * (576 + 512) * selected
 
 
-def test_stage_kernels_name_the_sliced_top_k():
+def test_stage_kernels_name_the_top_k_kernel():
     assert bench.stage_kernels(C2, 0)[1] == "topk_kernel"
+    assert bench.stage_kernels(C2, 0, 256)[1] == "topk_cand_kernel"       # candidate lists
+    assert bench.stage_kernels(C4, 0, 128)[1] == "topk_cand_kernel"
+    for k in bench.stage_kernels(C2, 0, 256):
+        assert k in bench.KERNELS
     assert bench.stage_kernels(C4, 4096)[1] == "tk_coop_kernel"            # 8 rows x 32 slices
     from dsa_workloads import scaled
     many = scaled(C4, batch=64)                                            # 2048 slices: three kernels

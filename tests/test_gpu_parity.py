@@ -196,13 +196,15 @@ def test_topk_special_rows(kind, Lk, K):
 
 @pytest.mark.parametrize("B,Lq,Lk", [(2, 1, 65536), (3, 1, 70001), (1, 1, 131072), (1, 3, 100000), (2, 2, 80000)])
 def test_sliced_topk_in_forward_equals_one_workgroup_per_row(B, Lq, Lk):
-    """Few rows of 65536 positions or more: dsa_forward selects with one
-    work-group per row slice.  Its indices must equal the one-work-group-per-row
-    selection of dsa_topk over the same scores, bit for bit."""
+    """Few rows of 65536 positions or more with K beyond the indexer's
+    candidate lists (8192): dsa_forward selects with one work-group per row
+    slice.  Its indices must equal the one-work-group-per-row selection of
+    dsa_topk over the same scores, bit for bit."""
     dsa = _dsa()
-    cfg = C.scaled(C.DECODE_32K, batch=B, q_len=Lq, kv_len=Lk, plant_count=min(300, Lk // 100))
+    cfg = C.scaled(C.DECODE_32K, batch=B, q_len=Lq, kv_len=Lk, topk=8192, plant_count=min(300, Lk // 100))
     inp = generate(cfg, device=DEV)
     p = dsa.make_problem(cfg)
+    assert dsa.topk_slice_len(p) > 0 and dsa.topk_list_slots(p) == 0
     scores = dsa.index_scores(p, inp["q_idx"], inp["q_scale"], inp["k_idx"], inp["k_scale"], inp["head_w"])
     single = dsa.topk(p, scores)
     idx = torch.empty(B, Lq, cfg.topk, dtype=torch.int32, device=DEV)
@@ -336,9 +338,11 @@ def test_forward_edge_shapes(case):
     # 2048-entry windows (more splits)
     dict(name="k5000_decode", batch=2, q_len=1, kv_len=9000, topk=5000),
     dict(name="k5000_prefill", batch=1, q_len=6, kv_len=7000, topk=5000),
-    # sliced top-k (>= 65536 positions) with spare cache capacity
-    dict(name="sliced_topk_capacity", batch=2, q_len=1, kv_len=70001, capacity=70100),
-    # FP8 index at 128K context: FP8 scores, sliced top-k, 16 splits
+    # top-k from the indexer's candidate lists with spare cache capacity
+    dict(name="lists_topk_capacity", batch=2, q_len=1, kv_len=70001, capacity=70100),
+    # sliced top-k (>= 65536 positions, K beyond the lists) with spare capacity
+    dict(name="sliced_topk_capacity", batch=2, q_len=1, kv_len=70001, capacity=70100, topk=5000),
+    # FP8 index at 128K context: FP8 scores and candidate lists, 16 splits
     dict(name="fp8_128k", batch=1, q_len=1, kv_len=131072, fp8=True),
 ])
 def test_forward_wide_cases(case):

@@ -76,12 +76,14 @@ def test_sliced_topk_special_rows(kind, Lk, K):
 
 @pytest.mark.parametrize("B,Lq,Lk", [(8, 1, 131072), (2, 1, 70001), (2, 3, 66000), (1, 1, 100000), (16, 1, 65536)])
 def test_forward_sliced_topk_equals_single_workgroup(B, Lq, Lk):
-    """dsa_forward's indices (sliced selection on its own scores) equal the
-    one-work-group-per-row selection of dsa_topk over the same scores."""
+    """dsa_forward's indices (sliced selection on its own scores: K = 6000
+    is beyond the indexer's candidate lists) equal the one-work-group-per-row
+    selection of dsa_topk over the same scores."""
     dsa = _dsa()
-    cfg = C.scaled(C.DECODE_32K, batch=B, q_len=Lq, kv_len=Lk, plant_count=min(300, Lk // 100))
+    cfg = C.scaled(C.DECODE_32K, batch=B, q_len=Lq, kv_len=Lk, topk=6000, plant_count=min(300, Lk // 100))
     inp = generate(cfg, device=DEV)
     p = dsa.make_problem(cfg)
+    assert dsa.topk_slice_len(p) > 0 and dsa.topk_list_slots(p) == 0
     scores = dsa.index_scores(p, inp["q_idx"], inp["q_scale"], inp["k_idx"], inp["k_scale"], inp["head_w"])
     single = dsa.topk(p, scores)
     idx = torch.empty(B, Lq, cfg.topk, dtype=torch.int32, device=DEV)

@@ -62,25 +62,32 @@ def _same(cfg, with_idx=True):
     assert torch.equal(l0, l1), cfg.name
     if with_idx:
         assert torch.equal(i0, i1), cfg.name
-    return dsa.topk_slice_len(p)
+    return dsa.topk_list_slots(p), dsa.topk_slice_len(p)
 
 
-SMALL_SLICED = C.scaled(C.DECODE_128K, name="decode_bf16_B2_ctx70001", batch=2, kv_len=70001)
+# top-k plans: candidate lists (16 or more 2048-key chunks), sliced (few
+# long rows with K beyond the lists), one work-group per row (short rows)
+SMALL_LISTS = C.scaled(C.DECODE_32K, name="decode_bf16_B2_ctx40000", batch=2, kv_len=40000)
+SMALL_SLICED = C.scaled(C.DECODE_128K, name="decode_bf16_B2_ctx70001_K8192", batch=2, kv_len=70001, topk=8192)
 SMALL_DECODE = C.scaled(C.DECODE_32K, name="decode_bf16_B4_ctx9000", batch=4, kv_len=9000)
 
 
-def test_static_forward_decode_32k_then_smaller_sliced():
-    # 32 x 32K (one work-group per top-k row), then 2 x 70001 (sliced top-k)
-    assert _same(C.DECODE_32K) == 0
-    assert _same(SMALL_SLICED) > 0
+def test_static_forward_decode_32k_then_smaller():
+    # 32 x 32K (candidate lists), then 2 x 70001 with K = 8192 (sliced
+    # top-k) and 2 x 40000 (lists again, over the sliced selection's state)
+    assert _same(C.DECODE_32K) == (256, 0)
+    lists, sl = _same(SMALL_SLICED)
+    assert lists == 0 and sl > 0
+    assert _same(SMALL_LISTS) == (256, 0)
 
 
 def test_static_forward_decode_128k_then_smaller():
-    # 8 x 128K (sliced top-k: histograms and barrier counters left in the
-    # scratch), then 2 x 70001 sliced again and 4 x 9000 without indices out
-    assert _same(C.DECODE_128K) > 0
-    assert _same(SMALL_SLICED) > 0
-    _same(SMALL_DECODE, with_idx=False)
+    # 8 x 128K (candidate lists of 128 slots left in the scratch), then
+    # 2 x 70001 sliced, 2 x 40000 with lists and 4 x 9000 without indices out
+    assert _same(C.DECODE_128K) == (128, 0)
+    assert _same(SMALL_SLICED)[1] > 0
+    assert _same(SMALL_LISTS)[0] == 256
+    assert _same(SMALL_DECODE, with_idx=False) == (0, 0)
 
 
 SMALL_PREFILL = C.scaled(C.PREFILL_8K, name="prefill_bf16_L300_ctx700", batch=2, q_len=300, kv_len=700)
