@@ -132,6 +132,27 @@ __device__ __forceinline__ void lds_dma_u8(const void* gbase, uint32_t voff, uin
 }
 #pragma clang diagnostic pop
 
+// DPP source shift within rows of 16 lanes (lanes whose source is out of
+// range read 0).
+template <int CTRL, int ROWS>
+__device__ __forceinline__ uint32_t dpp(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, ROWS, 0xf, false);
+}
+
+// Inclusive scan over the 64 lanes: shifts by 1, 2, 4, 8 within each row of
+// 16 lanes, then row 0's total into row 1 and row 2's into row 3
+// (row_bcast:15), then lane 31's running total into rows 2 and 3
+// (row_bcast:31).
+__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t v) {
+  v += dpp<0x111, 0xf>(v);
+  v += dpp<0x112, 0xf>(v);
+  v += dpp<0x114, 0xf>(v);
+  v += dpp<0x118, 0xf>(v);
+  v += dpp<0x142, 0xa>(v);
+  v += dpp<0x143, 0xc>(v);
+  return v;
+}
+
 // Order-preserving 32-bit key of a score, as the top-k kernels rank them:
 // larger score, larger key; -0.0 maps like +0.0.  Key 0 is reserved for
 // "no element" (slots past a row's end): real scores map to >= 1 (only the

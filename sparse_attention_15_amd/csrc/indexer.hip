@@ -196,22 +196,6 @@ __device__ __forceinline__ float reduce4(float p0, float p1, float p2, float p3)
 }
 
 // ------------------------------------------- decode: candidate lists -------
-// Inclusive scan over a wave's 64 lanes (DPP row shifts 1, 2, 4, 8, then the
-// row_bcast:15 and row_bcast:31 steps).
-template <int CTRL, int ROWS>
-__device__ __forceinline__ uint32_t dpp_shift(uint32_t v) {
-  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, ROWS, 0xf, false);
-}
-__device__ __forceinline__ uint32_t wave_scan_incl(uint32_t v) {
-  v += dpp_shift<0x111, 0xf>(v);
-  v += dpp_shift<0x112, 0xf>(v);
-  v += dpp_shift<0x114, 0xf>(v);
-  v += dpp_shift<0x118, 0xf>(v);
-  v += dpp_shift<0x142, 0xa>(v);
-  v += dpp_shift<0x143, 0xc>(v);
-  return v;
-}
-
 // The chunk's candidate list for the filtered top-k (256 threads; the
 // chunk's nk scores in sc; hist: 4096 + 8 words of free LDS).  Every
 // visible key of the chunk whose 12-bit key prefix (sign, exponent, three
@@ -258,7 +242,7 @@ __device__ void chunk_candidates(const IndexLaunch& a, int row, int nk, const fl
     uint32_t tot = 0u;
 #pragma unroll
     for (int j = 0; j < 16; ++j) tot += c[j];
-    const uint32_t incl = wave_scan_incl(tot);
+    const uint32_t incl = wave_incl_scan(tot);
     if (lane == 63) red[4 + wave] = incl;
     __syncthreads();
     uint32_t run = incl - tot;                   // keys in the bins above mine
@@ -280,7 +264,7 @@ __device__ void chunk_candidates(const IndexLaunch& a, int row, int nk, const fl
 #pragma unroll
   for (int e = 0; e < 8; ++e) take |= (k[e] != 0u && (int)(k[e] >> 20) > cut) ? (1u << e) : 0u;
   const uint32_t cnt = __builtin_popcount(take);
-  const uint32_t incl = wave_scan_incl(cnt);
+  const uint32_t incl = wave_incl_scan(cnt);
   if (lane == 63) red[4 + wave] = incl;
   __syncthreads();
   uint32_t off = incl - cnt, total = 0u;

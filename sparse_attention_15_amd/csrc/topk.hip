@@ -41,26 +41,6 @@ constexpr int kWaves = kThreads / 64;
 constexpr int kBins = 4096;
 constexpr int kGroup = 8;            // chunks per emission group
 
-// DPP source shift (lanes whose source is out of range read 0).
-template <int CTRL, int ROWS>
-__device__ __forceinline__ uint32_t dpp(uint32_t v) {
-  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, ROWS, 0xf, false);
-}
-
-// Inclusive scan over the 64 lanes: shifts by 1, 2, 4, 8 within each row of
-// 16 lanes, then row 0's total into row 1 and row 2's into row 3
-// (row_bcast:15), then lane 31's running total into rows 2 and 3
-// (row_bcast:31).
-__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t v) {
-  v += dpp<0x111, 0xf>(v);
-  v += dpp<0x112, 0xf>(v);
-  v += dpp<0x114, 0xf>(v);
-  v += dpp<0x118, 0xf>(v);
-  v += dpp<0x142, 0xa>(v);
-  v += dpp<0x143, 0xc>(v);
-  return v;
-}
-
 template <int NC, int C>
 struct Shared {
   static constexpr int kStride = kBins + 4;   // bin j, copy c at c * kStride + j

@@ -56,23 +56,6 @@ __device__ __forceinline__ uint32_t skey(float x) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-template <int CTRL, int ROWS>
-__device__ __forceinline__ uint32_t dpp(uint32_t v) {
-  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, ROWS, 0xf, false);
-}
-
-// Inclusive scan over a wave's 64 lanes (row shifts 1, 2, 4, 8, then the
-// row_bcast:15 and row_bcast:31 steps).
-__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t v) {
-  v += dpp<0x111, 0xf>(v);
-  v += dpp<0x112, 0xf>(v);
-  v += dpp<0x114, 0xf>(v);
-  v += dpp<0x118, 0xf>(v);
-  v += dpp<0x142, 0xa>(v);
-  v += dpp<0x143, 0xc>(v);
-  return v;
-}
-
 // Exclusive block-wide scan of one value per thread; *total gets the sum.
 // ws holds kW words of scratch.  All threads must call; contains barriers.
 __device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t* ws, uint32_t* total) {
