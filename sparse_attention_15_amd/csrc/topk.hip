@@ -507,8 +507,10 @@ __global__ __launch_bounds__(kThreads, NC == 2 ? 8 : 4) void topk_kernel(TopkLau
 // past each list's count.  A radix select over the listed keys finds their
 // K-th largest, T'.  When T''s 12-bit prefix lies above every chunk's cutoff
 // bin, every key >= T' of the row is listed, so T' is the row's K-th largest
-// key and the listed keys alone decide the selection; the chosen positions
-// then leave in slot order.  Otherwise (or with fewer than K keys listed)
+// key and the listed keys alone decide the selection; each thread then
+// stores its chosen positions straight to their output slots (a few
+// thousand 4-byte stores per row: staging them in LDS for 16-byte stores
+// costs a barrier and measured slower).  Otherwise (or with fewer than K keys listed)
 // the work-group selects from the full row of scores, NCF chunks per thread
 // in registers.
 template <int NCF>
@@ -657,18 +659,11 @@ __global__ __launch_bounds__(kThreads, 4) void topk_cand_kernel(TopkLaunch a) {
         const uint32_t slot = g_b + min(e_b, quota);
         const int q = 4 * c + e;
         const int pos = pos0 + (int)((offs[q >> 1] >> (16 * (q & 1))) & 0xffffu);
-        if (slot < (uint32_t)K) sh.hist[slot] = (uint32_t)pos;   // always, by construction
+        if (slot < (uint32_t)K) out[slot] = pos;  // always, by construction
       }
       g_b += gt ? 1u : 0u;
       e_b += eq ? 1u : 0u;
     }
-  __syncthreads();
-  if ((K & 3) == 0 && (reinterpret_cast<uintptr_t>(out) & 15u) == 0) {
-    for (int j = tid; j < K / 4; j += kThreads)
-      st16(out + 4 * j, u32x4{sh.hist[4 * j], sh.hist[4 * j + 1], sh.hist[4 * j + 2], sh.hist[4 * j + 3]});
-  } else {
-    for (int j = tid; j < K; j += kThreads) out[j] = (int32_t)sh.hist[j];
-  }
 }
 
 }  // namespace
