@@ -4,7 +4,7 @@
 
 Every call recompiles every source (objects go to _build/, the library next
 to this file).  Sources are compiled for gfx950 only, with packed-fp32 code
-generation disabled.
+generation disabled and implicit 64 -> 32-bit narrowing rejected.
 """
 from __future__ import annotations
 
@@ -28,6 +28,10 @@ COMMON_FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wno-unused-command-line-argument",
+    # an implicit 64 -> 32-bit narrowing is an error: the wave builtins
+    # (readfirstlane and the like) take 32-bit values, and a pointer passed
+    # to one silently loses its upper half
+    "-Werror=shorten-64-to-32",
     f"-I{INCLUDE}", f"-I{CSRC}",
 ]
 
