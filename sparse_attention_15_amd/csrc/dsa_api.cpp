@@ -10,6 +10,8 @@
 
 using namespace dsa;
 
+thread_local StageEvents dsa::g_stage_events = {nullptr, nullptr};
+
 namespace {
 
 constexpr size_t kAlign = 256;
@@ -204,7 +206,10 @@ dsa_status_t check_attn_ptrs(const void* qa, const void* kv, const void* out) {
   return DSA_OK;
 }
 
-// Records events[slot*2 + which] if that slot exists.
+// Times stage `stage` of chunk `chunk` with events[slot*2], events[slot*2+1]
+// if that slot exists: rec(.., 0) attaches them to the stage's launches (the
+// first kernel's start, the last kernel's end); rec(.., 1) records both by
+// themselves if the stage launched nothing.
 struct EventSink {
   hipEvent_t* ev;
   int n_slots;
@@ -212,7 +217,16 @@ struct EventSink {
   hipError_t rec(int chunk, int stage, int which) const {
     const int slot = chunk * DSA_NUM_STAGES + stage;
     if (!ev || slot >= n_slots) return hipSuccess;
-    return hipEventRecord(ev[2 * slot + which], s);
+    if (which == 0) {
+      g_stage_events = StageEvents{ev[2 * slot], ev[2 * slot + 1]};
+      return hipSuccess;
+    }
+    hipError_t e = hipSuccess;
+    if (g_stage_events.start) {                   // nothing was launched
+      if ((e = hipEventRecord(ev[2 * slot], s)) == hipSuccess) e = hipEventRecord(ev[2 * slot + 1], s);
+    }
+    g_stage_events = StageEvents{nullptr, nullptr};
+    return e;
   }
 };
 
@@ -220,6 +234,9 @@ dsa_status_t forward_impl(const dsa_problem_t* prob, const void* q_idx, const ui
                           const uint8_t* k_scale, const float* head_w, const void* q_attn, const void* kv,
                           int32_t* topk_idx, void* out, float* lse, void* workspace, size_t workspace_bytes,
                           const EventSink& ev, int32_t* n_chunks_out, hipStream_t stream) {
+  struct StageReset {                             // no stage timing outlives the call, on any return
+    ~StageReset() { g_stage_events = StageEvents{nullptr, nullptr}; }
+  } stage_reset;
   Path path;
   dsa_status_t st = check_problem(prob, &path);
   if (st != DSA_OK) return st;

@@ -1,6 +1,7 @@
 // Internal launch interface between the C-ABI front end (dsa_api.cpp) and
 // the kernel translation units.  Host-only declarations.
 #pragma once
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 #include <stddef.h>
@@ -154,5 +155,26 @@ int gemm_ksplit(int M, int N, int K, int batch, size_t* bytes);
 
 // Split count the bf16 attention uses for a launch of `rows` queries.
 int attn_splits_bf16(int rows, int K);
+
+// Optional timing of a stage's launches, set by the timed forward on the
+// launching host thread: the next launch records `start` as its kernel
+// begins, and every launch records `stop` as its kernel ends, so the pair
+// brackets the stage's kernels (no separate event packets between them).
+struct StageEvents {
+  hipEvent_t start, stop;
+};
+extern thread_local StageEvents g_stage_events;
+
+// Every kernel of the path launches through here.
+template <typename F, typename... Args>
+inline void launch_kernel(F kernel, dim3 grid, dim3 block, size_t smem, hipStream_t s, Args... args) {
+  StageEvents& ev = g_stage_events;
+  if (ev.start || ev.stop) {
+    hipExtLaunchKernelGGL(kernel, grid, block, (uint32_t)smem, s, ev.start, ev.stop, 0, args...);
+    ev.start = nullptr;
+  } else {
+    hipLaunchKernelGGL(kernel, grid, block, smem, s, args...);
+  }
+}
 
 }  // namespace dsa

@@ -572,7 +572,7 @@ hipError_t launch_mfma(const IndexLaunch& a, hipStream_t s) {
     if (a.cand_m && (a.cand_m > kCandCap || (a.cand_m & 7) || !a.cand_keys || !a.cand_offs || !a.cand_hdr))
       return hipErrorInvalidValue;
     dim3 grid((a.Lk + kDecChunk - 1) / kDecChunk, a.B * a.q_count);
-    hipLaunchKernelGGL(idx_decode_kernel<FP8>, grid, dim3(256), 0, s, a);
+    launch_kernel(idx_decode_kernel<FP8>, grid, dim3(256), 0, s, a);
   } else {
     // only the decode kernel clears zero_hist and writes candidate lists
     if (a.zero_hist || a.cand_m) return hipErrorInvalidValue;
@@ -581,7 +581,7 @@ hipError_t launch_mfma(const IndexLaunch& a, hipStream_t s) {
     const int n_max = a.Lk - a.Lq + a.q_begin + a.q_count;
     const int ks = pick_ksplit(nqb * a.B, (n_max + 63) / 64);
     dim3 grid(nqb, ks, a.B);
-    hipLaunchKernelGGL((idx_prefill_kernel<FP8, QB>), grid, dim3(QB * 64), 0, s, a, ks);
+    launch_kernel(idx_prefill_kernel<FP8, QB>, grid, dim3(QB * 64), 0, s, a, ks);
   }
   return hipGetLastError();
 }
@@ -592,7 +592,7 @@ hipError_t launch_index_f32(const IndexLaunch& a, hipStream_t s) {
   if (a.zero_hist || a.cand_m) return hipErrorInvalidValue;   // decode kernel only
   dim3 grid((a.Lk + 255) / 256, a.B * a.q_count);
   const size_t smem = (size_t)(a.H * a.D + a.H) * sizeof(float);
-  hipLaunchKernelGGL(idx_f32_kernel, grid, dim3(256), smem, s, a);
+  launch_kernel(idx_f32_kernel, grid, dim3(256), smem, s, a);
   return hipGetLastError();
 }
 

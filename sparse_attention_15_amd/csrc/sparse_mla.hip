@@ -788,9 +788,9 @@ hipError_t launch_attn_bf16(const AttnLaunch& a, hipStream_t s) {
   dim3 grid(a.splits, a.B * a.q_count);
   const int per = ((a.K + a.splits - 1) / a.splits + kBK - 1) / kBK * kBK;
   if (per <= 256)
-    hipLaunchKernelGGL((attn_bf16_kernel<4, 256>), grid, dim3(kWavesA * 64), 0, s, a);
+    launch_kernel(attn_bf16_kernel<4, 256>, grid, dim3(kWavesA * 64), 0, s, a);
   else
-    hipLaunchKernelGGL((attn_bf16_kernel<3, kMaxPer>), grid, dim3(kWavesA * 64), 0, s, a);
+    launch_kernel(attn_bf16_kernel<3, kMaxPer>, grid, dim3(kWavesA * 64), 0, s, a);
   return hipGetLastError();
 }
 
@@ -799,11 +799,11 @@ hipError_t launch_combine_vt(const AttnLaunch& a, hipStream_t s) {
   dim3 grid(4 * (kVTiles / VT), a.B * a.q_count);
   dim3 block(128 * VT);
   switch (a.splits) {
-    case 2: hipLaunchKernelGGL((attn_combine_kernel<2, F32, VT>), grid, block, 0, s, a); break;
-    case 4: hipLaunchKernelGGL((attn_combine_kernel<4, F32, VT>), grid, block, 0, s, a); break;
-    case 8: hipLaunchKernelGGL((attn_combine_kernel<8, F32, VT>), grid, block, 0, s, a); break;
-    case 16: hipLaunchKernelGGL((attn_combine_kernel<16, F32, VT>), grid, block, 0, s, a); break;
-    case 32: hipLaunchKernelGGL((attn_combine_kernel<32, F32, VT>), grid, block, 0, s, a); break;
+    case 2: launch_kernel(attn_combine_kernel<2, F32, VT>, grid, block, 0, s, a); break;
+    case 4: launch_kernel(attn_combine_kernel<4, F32, VT>, grid, block, 0, s, a); break;
+    case 8: launch_kernel(attn_combine_kernel<8, F32, VT>, grid, block, 0, s, a); break;
+    case 16: launch_kernel(attn_combine_kernel<16, F32, VT>, grid, block, 0, s, a); break;
+    case 32: launch_kernel(attn_combine_kernel<32, F32, VT>, grid, block, 0, s, a); break;
     default: return hipErrorInvalidValue;       // splits are powers of two up to 32
   }
   return hipGetLastError();
@@ -824,7 +824,7 @@ hipError_t launch_attn_combine(const AttnLaunch& a, hipStream_t s) {
 hipError_t launch_attn_f32(const AttnLaunch& a, hipStream_t s) {
   dim3 grid(a.NH, a.B * a.q_count);
   const size_t smem = (size_t)(a.Dqk + a.K) * sizeof(float);
-  hipLaunchKernelGGL(attn_f32_kernel, grid, dim3(256), smem, s, a);
+  launch_kernel(attn_f32_kernel, grid, dim3(256), smem, s, a);
   return hipGetLastError();
 }
 

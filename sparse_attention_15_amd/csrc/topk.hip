@@ -679,15 +679,15 @@ void launch_rows(const TopkLaunch& a, int n_max, int grid, hipStream_t s) {
   // fit two work-groups per CU (64K FP8 prefill: top-k 4.30 -> 3.96 ms per
   // step); a decode batch of such rows keeps 8.
   if (iters <= 2)
-    hipLaunchKernelGGL((topk_kernel<2, 2>), dim3(grid), dim3(kThreads), 0, s, a);
+    launch_kernel(topk_kernel<2, 2>, dim3(grid), dim3(kThreads), 0, s, a);
   else if (iters <= 8 && grid >= 512)
-    hipLaunchKernelGGL((topk_kernel<8, 4>), dim3(grid), dim3(kThreads), 0, s, a);
+    launch_kernel(topk_kernel<8, 4>, dim3(grid), dim3(kThreads), 0, s, a);
   else if (iters <= 8)
-    hipLaunchKernelGGL((topk_kernel<8, 8>), dim3(grid), dim3(kThreads), 0, s, a);
+    launch_kernel(topk_kernel<8, 8>, dim3(grid), dim3(kThreads), 0, s, a);
   else if (iters <= 16)
-    hipLaunchKernelGGL((topk_kernel<16, 8>), dim3(grid), dim3(kThreads), 0, s, a);
+    launch_kernel(topk_kernel<16, 8>, dim3(grid), dim3(kThreads), 0, s, a);
   else
-    hipLaunchKernelGGL((topk_kernel<0, 8>), dim3(grid), dim3(kThreads), 0, s, a);
+    launch_kernel(topk_kernel<0, 8>, dim3(grid), dim3(kThreads), 0, s, a);
 }
 
 }  // namespace
@@ -724,11 +724,11 @@ hipError_t launch_topk_cand(const TopkLaunch& a, hipStream_t s) {
   // the full-row fallback keeps rows of up to 65536 positions in registers
   const int iters = ((n_max + 3) / 4 + kThreads - 1) / kThreads;
   if (iters <= 8)
-    hipLaunchKernelGGL((topk_cand_kernel<8>), dim3(rows), dim3(kThreads), 0, s, a);
+    launch_kernel(topk_cand_kernel<8>, dim3(rows), dim3(kThreads), 0, s, a);
   else if (iters <= 16)
-    hipLaunchKernelGGL((topk_cand_kernel<16>), dim3(rows), dim3(kThreads), 0, s, a);
+    launch_kernel(topk_cand_kernel<16>, dim3(rows), dim3(kThreads), 0, s, a);
   else
-    hipLaunchKernelGGL((topk_cand_kernel<0>), dim3(rows), dim3(kThreads), 0, s, a);
+    launch_kernel(topk_cand_kernel<0>, dim3(rows), dim3(kThreads), 0, s, a);
   return hipGetLastError();
 }
 

@@ -762,15 +762,15 @@ __global__ __launch_bounds__(kT) void tk_zero_kernel(uint32_t* p, int64_t n4) {
 template <int CPT, bool VEC>
 void launch_sliced_t(const TopkLaunch& a, hipStream_t s) {
   const int grid = a.B * a.q_count * a.sl_count;
-  hipLaunchKernelGGL((tk_hist_kernel<CPT, VEC>), dim3(grid), dim3(kT), 0, s, a);
-  hipLaunchKernelGGL((tk_classify_kernel<CPT, VEC>), dim3(grid), dim3(kT), 0, s, a);
-  hipLaunchKernelGGL(tk_emit_kernel, dim3(grid), dim3(kT), 0, s, a, CPT * 4 * kT);
+  launch_kernel(tk_hist_kernel<CPT, VEC>, dim3(grid), dim3(kT), 0, s, a);
+  launch_kernel(tk_classify_kernel<CPT, VEC>, dim3(grid), dim3(kT), 0, s, a);
+  launch_kernel(tk_emit_kernel, dim3(grid), dim3(kT), 0, s, a, CPT * 4 * kT);
 }
 
 template <int CPT, bool VEC>
 void launch_coop_t(const TopkLaunch& a, hipStream_t s) {
   const int grid = a.B * a.q_count * a.sl_count;
-  hipLaunchKernelGGL((tk_coop_kernel<CPT, VEC>), dim3(grid), dim3(kT), 0, s, a);
+  launch_kernel(tk_coop_kernel<CPT, VEC>, dim3(grid), dim3(kT), 0, s, a);
 }
 
 // Work-groups of tk_coop_kernel<CPT, VEC> the current device holds at once
@@ -841,7 +841,7 @@ hipError_t launch_topk_sliced(const TopkLaunch& a, bool zero_hist, hipStream_t s
     return hipErrorInvalidValue;
   if (zero_hist) {
     const int64_t n4 = (int64_t)a.B * a.q_count * kHead / 4;
-    hipLaunchKernelGGL(tk_zero_kernel, dim3((unsigned)((n4 + kT - 1) / kT)), dim3(kT), 0, s, a.sl_hist, n4);
+    launch_kernel(tk_zero_kernel, dim3((unsigned)((n4 + kT - 1) / kT)), dim3(kT), 0, s, a.sl_hist, n4);
   }
   const hipError_t e = a.vec_ok ? launch_sliced_v<true>(a, s) : launch_sliced_v<false>(a, s);
   if (e != hipSuccess) return e;
